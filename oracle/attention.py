@@ -1,0 +1,250 @@
+"""Plain float64 attention on the CPU (test infrastructure only; see package doc).
+
+Nothing here is blocked, fused or reordered beyond what the definition
+states: for each (batch, query head) the full score rows S are formed with a
+matrix product, masked, exponentiated, normalised into P and multiplied by V.
+Row blocks of at most ``row_block`` queries only bound memory; each block
+still forms complete rows of S.
+"""
+
+import math
+
+import numpy as np
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def key_visibility(Lq, Lk, causal, window_left=-1, window_right=-1, rows=None):
+    """Boolean matrix vis[r, j]: is key j visible to query row rows[r]?
+
+    Masking rules: the causal mask of autoregressive inference ("FlashAttention-3
+    vs naive attention", sec. 1.1 and 2.1) and the sliding window
+    ``window_size=(left, right)`` of the configuration skill page (sec. 3.3,
+    where (4096, 0) means looking back 4096 tokens).  Readings taken where the
+    pages are silent: query row i sits at absolute key position i + (Lk - Lq)
+    (bottom-right alignment, so a one-token decode query sees its whole
+    history); window bounds are inclusive; a negative side is unbounded.
+    """
+    i = np.arange(Lq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    pos = i[:, None] + (Lk - Lq)
+    j = np.arange(Lk, dtype=np.int64)[None, :]
+    vis = np.ones((i.shape[0], Lk), dtype=bool)
+    if causal:
+        vis &= j <= pos
+    if window_left >= 0:
+        vis &= j >= pos - window_left
+    if window_right >= 0:
+        vis &= j <= pos + window_right
+    return vis
+
+
+def attend_rows(q_rows, k, v, scale, vis):
+    """Standard attention for a block of query rows of one head.
+
+    "FlashAttention-3 vs naive attention", sec. 1.1: S = scale * Q K^T (+mask),
+    P = softmax(S), O = P V.  Softmax is the usual max-subtracted form (same
+    page, sec. 6.1).  Returns O (n, dv), LSE (n,) with LSE = m + ln l, and P
+    (n, Lk).  Rows with no visible key give O = 0, LSE = -inf, P = 0.
+    """
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+    s = scale * (q_rows @ k.T)                      # S, materialised
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1) if s.shape[1] > 0 else np.full(s.shape[0], -np.inf)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe[:, None])                 # masked entries -> exp(-inf) = 0
+    l = e.sum(axis=1)
+    ok = l > 0
+    p = np.zeros_like(e)
+    p[ok] = e[ok] / l[ok, None]                     # P, materialised
+    lse = np.full(l.shape, -np.inf)
+    lse[ok] = m_safe[ok] + np.log(l[ok])
+    o = p @ v
+    return o, lse, p
+
+
+def _kv_head(h, Hq, Hkv):
+    """GQA/MQA broadcast ("flash-attention" skill page, appendix on GQA/MQA):
+    Hkv divides Hq and query heads [g*G, (g+1)*G) share KV head g, G = Hq/Hkv
+    (the repeat_kv / repeat_interleave convention)."""
+    if Hq % Hkv != 0:
+        raise ValueError("Hkv must divide Hq")
+    return h // (Hq // Hkv)
+
+
+def attention_rows_ref(q, k, v, b, h, rows, softmax_scale=None, causal=False,
+                       window=(-1, -1), return_probs=False):
+    """Selected query rows of one (batch b, query head h) of dense attention.
+
+    q: (B, Lq, Hq, d); k, v: (B, Lk, Hkv, d).  Returns O (n, d), LSE (n,)
+    (and P (n, Lk) if asked).  Used to check sampled rows at full size.
+    """
+    B, Lq, Hq, d = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    g = _kv_head(h, Hq, Hkv)
+    rows = np.asarray(rows, dtype=np.int64)
+    vis = key_visibility(Lq, Lk, causal, window[0], window[1], rows=rows)
+    o, lse, p = attend_rows(_f64(q[b, rows, h, :]), _f64(k[b, :, g, :]),
+                            _f64(v[b, :, g, :]), scale, vis)
+    return (o, lse, p) if return_probs else (o, lse)
+
+
+def attention_ref(q, k, v, softmax_scale=None, causal=False, window=(-1, -1),
+                  row_block=1024):
+    """Dense attention over (B, L, H, d) tensors, the layout of the skill
+    page's flash_attn_func (sec. 3.1/3.2); default scale 1/sqrt(headdim).
+
+    Returns O (B, Lq, Hq, d) float64 and LSE (B, Hq, Lq) float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Lq, Hq, d = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Lk, Hkv, d) or v.shape[:3] != (B, Lk, Hkv):
+        raise ValueError("q/k/v shapes disagree")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    O = np.zeros((B, Lq, Hq, v.shape[3]))
+    LSE = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            kk, vv = k[b, :, g, :], v[b, :, g, :]
+            for r0 in range(0, Lq, row_block):
+                rows = np.arange(r0, min(Lq, r0 + row_block))
+                vis = key_visibility(Lq, Lk, causal, window[0], window[1], rows=rows)
+                o, lse, _ = attend_rows(q[b, rows, h, :], kk, vv, scale, vis)
+                O[b, rows, h, :] = o
+                LSE[b, h, rows] = lse
+    return O, LSE
+
+
+def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale=None,
+                         causal=False, window=(-1, -1), row_block=1024):
+    """Packed variable-length attention (skill page sec. 3.4 and the appendix on
+    continuous batching): sequences are concatenated along the token axis,
+    cu_seqlens holds batch+1 cumulative offsets, and no token attends across
+    sequences.  Each sequence is the dense definition on its own slice.
+
+    q: (total_q, Hq, d); k, v: (total_k, Hkv, d).  Returns O (total_q, Hq, d)
+    and LSE (Hq, total_q).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    Hq = q.shape[1]
+    O = np.zeros((q.shape[0], Hq, v.shape[2]))
+    LSE = np.full((Hq, q.shape[0]), -np.inf)
+    for b in range(len(cq) - 1):
+        qs, qe, ks, ke = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if qe == qs:
+            continue
+        o, lse = attention_ref(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke],
+                               softmax_scale, causal, window, row_block)
+        O[qs:qe] = o[0]
+        LSE[:, qs:qe] = lse[0]
+    return O, LSE
+
+
+def gather_paged(cache, block_table_row, length, page_size):
+    """Read the first ``length`` key rows of one sequence out of a paged cache.
+
+    Paged KV ("flash-attention" skill page, appendix on PagedAttention, and the
+    "FIA / FlashAttention" explainer, sec. 2): the cache is
+    [num_pages, page_size, Hkv, d]; token j of the sequence lives in page
+    block_table[j // page_size], slot j % page_size.
+    """
+    j = np.arange(length, dtype=np.int64)
+    pages = np.asarray(block_table_row, dtype=np.int64)[j // page_size]
+    return cache[pages, j % page_size]                # (length, Hkv, d)
+
+
+def decode_paged_ref(q, k_cache, v_cache, block_table, cache_seqlens, page_size,
+                     softmax_scale=None, window_left=-1):
+    """One decode step over a paged KV cache ("flash-attention" skill page,
+    appendix on PagedAttention / FlashDecoding; "FlashAttention-3 vs naive
+    attention", sec. 2.2): each request's single query row attends to its
+    cache_seqlens[b] cached tokens (all visible under bottom-right causal
+    alignment; a left window keeps the last window_left + 1).
+
+    q: (B, 1, Hq, d); caches [num_pages, page_size, Hkv, d].  Returns
+    O (B, 1, Hq, d) and LSE (B, Hq).
+    """
+    q = _f64(q)
+    B, _, Hq, d = q.shape
+    O = np.zeros((B, 1, Hq, d))
+    LSE = np.zeros((B, Hq))
+    for b in range(B):
+        n = int(cache_seqlens[b])
+        kk = _f64(gather_paged(k_cache, block_table[b], n, page_size))[None]
+        vv = _f64(gather_paged(v_cache, block_table[b], n, page_size))[None]
+        o, lse = attention_ref(q[b:b + 1], kk, vv, softmax_scale, causal=True,
+                               window=(window_left, -1))
+        O[b] = o[0]
+        LSE[b] = lse[0, :, 0]
+    return O, LSE
+
+
+def decode_split_partials_ref(q_row, k, v, scale, split_tokens, lo=0):
+    """Split-KV partial results for one decode query row ("flash-attention"
+    skill page, appendix on FlashDecoding / Split-KV: several workers take
+    different KV ranges of the same head and the results are reduced).
+
+    Keys [lo, len) are cut into chunks of ``split_tokens`` aligned to 0; each
+    chunk is plain attention over its keys, giving (lse_s, O_s).
+    """
+    n = k.shape[0]
+    lses, outs = [], []
+    for s0 in range(0, n, split_tokens):
+        ks = max(s0, lo)
+        ke = min(n, s0 + split_tokens)
+        if ke <= ks:
+            continue
+        vis = np.ones((1, ke - ks), dtype=bool)
+        o, lse, _ = attend_rows(_f64(q_row)[None], k[ks:ke], v[ks:ke], scale, vis)
+        lses.append(lse[0])
+        outs.append(o[0])
+    return np.array(lses), np.array(outs)
+
+
+def merge_partials_ref(lse_parts, o_parts):
+    """Reduce split partials into one row (the "online-softmax reduction" of the
+    FIA explainer, sec. 2, and the final reduce of split-KV on the skill page).
+
+    With M = max_s lse_s: LSE = M + ln sum_s exp(lse_s - M) and
+    O = sum_s exp(lse_s - LSE) * O_s.  Empty input or all -inf gives (-inf, 0).
+    """
+    lse_parts = _f64(lse_parts)
+    o_parts = _f64(o_parts)
+    if lse_parts.size == 0 or not np.isfinite(lse_parts).any():
+        dv = o_parts.shape[-1] if o_parts.ndim == 2 and o_parts.shape[-1] else 0
+        return -np.inf, np.zeros(dv)
+    M = lse_parts.max()
+    w = np.exp(lse_parts - M)
+    lse = M + math.log(w.sum())
+    o = (np.exp(lse_parts - lse)[:, None] * o_parts).sum(axis=0)
+    return lse, o
+
+
+def online_softmax_ref(q_row, k, v, scale, block):
+    """The streaming (online) softmax of the pages, written as its steps: keys
+    are visited in blocks; a running row max m and normaliser l are kept; when
+    a block raises the max, the old l and the output accumulator are rescaled by
+    exp(m_old - m_new) ("FIA / FlashAttention" explainer, sec. 1; glossary page,
+    "online normalization"; "FlashAttention-3 vs naive attention", sec. 6.2).
+
+    Returns (O, LSE) for one query row; O is divided by l once at the end.
+    """
+    q_row, k, v = _f64(q_row), _f64(k), _f64(v)
+    m = -np.inf
+    l = 0.0
+    acc = np.zeros(v.shape[1])
+    for j0 in range(0, k.shape[0], block):
+        s = scale * (k[j0:j0 + block] @ q_row)      # scores of this block
+        m_new = max(m, s.max())
+        alpha = math.exp(m - m_new) if np.isfinite(m) else 0.0
+        p = np.exp(s - m_new)
+        l = alpha * l + p.sum()
+        acc = alpha * acc + p @ v[j0:j0 + block]
+        m = m_new
+    return acc / l, m + math.log(l)
