@@ -1,0 +1,242 @@
+"""Benchmark of the fused attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one fa_fwd call on the causal MHA prefill workload (B=4, H=32,
+L=2048, d=128, bf16, seeded synthetic inputs resident in HBM).  The timed
+region is exactly K steps bracketed by torch.cuda.synchronize(); `value` is
+algorithmic TFLOP/s (4*d FLOPs per visible (query, key) pair per head).
+The other workloads (long-context GQA prefill, paged decode, varlen window
+prefill, the small dense case) are timed in the same run and reported under
+"workloads".  One JSON line is printed.
+
+"roofline" covers the dominant kernel (the prefill kernel on the main
+workload): achieved = algorithmic FLOPs per launch / the launch's average
+duration from HIP events on the launch stream, against the bf16 dense MFMA
+peak.  "traffic" comes from the committed rocprofv3 counter summary for that
+kernel and is null if the kernel source changed since it was taken.
+"cpu_baseline" times the CPU fp64 oracle on a bounded sample of the same
+workload on this host.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E (published)
+METRIC = "prefill attn TFLOP/s (% MFMA peak); paged-decode KV GB/s (% HBM peak)"
+PREFILL_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "prefill_fwd.hip")
+DECODE_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "decode_paged.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def visible_pairs(Lq, Lk, causal, wl, wr):
+    """Number of visible (query, key) pairs of one head (closed form per row)."""
+    i = np.arange(Lq, dtype=np.int64)
+    pos = i + (Lk - Lq)
+    lo = np.zeros(Lq, np.int64) if wl < 0 else np.maximum(0, pos - wl)
+    hi = np.full(Lq, Lk, np.int64)
+    if causal:
+        hi = np.minimum(hi, pos + 1)
+    if wr >= 0:
+        hi = np.minimum(hi, pos + wr + 1)
+    return int(np.maximum(0, hi - lo).sum())
+
+
+def dense_flops(w):
+    B, Lq, Hq, d = w.q.shape
+    return 4.0 * d * Hq * B * visible_pairs(Lq, w.k.shape[1], w.causal, *w.window)
+
+
+def varlen_flops(w):
+    d, H = w.q.shape[2], w.q.shape[1]
+    return 4.0 * d * H * sum(visible_pairs(int(L), int(L), w.causal, *w.window) for L in w.lens)
+
+
+def decode_bytes(w):
+    """Compulsory HBM bytes of one decode step: the used K/V rows once, q, o, lse,
+    and the used block-table entries."""
+    B, _, Hq, d = w.q.shape
+    Hkv = w.k_cache.shape[2]
+    tokens = int(w.seqlens.astype(np.int64).sum())
+    pages = int((-(-w.seqlens.astype(np.int64) // w.page_size)).sum())
+    return 2 * tokens * Hkv * d * 2 + 2 * B * Hq * d * 2 + B * Hq * 4 + pages * 4
+
+
+def file_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def time_calls(fn, steps, warmup):
+    """Average ms per call from HIP events recorded on the launch stream
+    (torch's current stream, which the binding launches on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def load_traffic(kernel_key, src):
+    try:
+        t = json.load(open(TRAFFIC_FILE))[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha256_16") != file_hash(src):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, flops_total):
+    """Time the CPU fp64 oracle on a bounded sample of the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    B, L, Hq, d = w.q.shape
+    pairs = [(b, h) for b in range(B) for h in range(Hq)][:32]
+    qb = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    kb = w.k.contiguous().view(torch.int16).numpy().view(np.uint16)
+    vb = w.v.contiguous().view(torch.int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    for b, h in pairs:
+        oracle.attention_rows_ref(qb, kb, vb, b, h, np.arange(L), w.scale, w.causal, w.window)
+    dt = time.perf_counter() - t0
+    sample_flops = flops_total * len(pairs) / (B * Hq)
+    return {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(pairs)} of {B * Hq} (batch, head) pairs of {w.name}, all {L} rows each, "
+                      "full S and P in float64 (numpy)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-main", action="store_true", help="time only the main workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import exact_attention_17_amd as fa
+    fa.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    props = torch.cuda.get_device_properties(0)
+
+    # ---------------------------------------------------------- main workload
+    w2 = workloads.causal_mha()
+    q, k, v = w2.q.cuda(), w2.k.cuda(), w2.v.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((4, 32, 2048), dtype=torch.float32, device="cuda")
+    step = lambda: fa.fa_fwd(q, k, v, w2.scale, True, (-1, -1), out=o, lse=lse)
+    flops2 = dense_flops(w2)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = time_calls(step, args.steps, 2)
+    value = flops2 / (wall_ms * 1e-3) / 1e12
+    achieved = flops2 / (ev_ms * 1e-3) / 1e12
+    traffic = load_traffic("prefill_fwd_causal_mha", PREFILL_SRC)
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w2.name, "B": 4, "Hq": 32, "Hkv": 32, "L": 2048, "d": 128,
+                   "causal": True, "flops_per_step": flops2},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "prefill_fwd_kernel<128,false>",
+                     "avg_launch_ms": round(ev_ms, 4)},
+        "device": props.name,
+    }
+    del q, k, v, o, lse
+
+    # ------------------------------------------------------- other workloads
+    wl = {}
+    if not args.only_main:
+        w1 = workloads.small_dense(Hkv=1)
+        a = [t.cuda() for t in (w1.q, w1.k, w1.v)]
+        ms = time_calls(lambda: fa.fa_fwd(*a, w1.scale, False), args.steps, args.warmup)
+        wl["small_dense"] = {"ms": round(ms, 4), "TFLOP/s": round(dense_flops(w1) / ms / 1e9, 3)}
+        del a
+
+        w3 = workloads.causal_gqa_long()
+        a = [t.cuda() for t in (w3.q, w3.k, w3.v)]
+        f3 = dense_flops(w3)
+        ms = time_calls(lambda: fa.fa_fwd(*a, w3.scale, True), max(5, args.steps // 5), 3)
+        wl["causal_gqa_long"] = {"ms": round(ms, 4), "TFLOP/s": round(f3 / ms / 1e9, 2),
+                                 "frac_mfma": round(f3 / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                 "flops": f3}
+        del a, w3
+
+        w5 = workloads.varlen_window()
+        a = [t.cuda() for t in (w5.q, w5.k, w5.v)]
+        cu = torch.from_numpy(w5.cu_seqlens).cuda()
+        f5 = varlen_flops(w5)
+        ms = time_calls(lambda: fa.fa_fwd_varlen(*a, cu, cu, w5.max_seqlen, w5.max_seqlen, w5.scale,
+                                                 True, w5.window), args.steps, args.warmup)
+        wl["varlen_window"] = {"ms": round(ms, 4), "TFLOP/s": round(f5 / ms / 1e9, 2),
+                               "frac_mfma": round(f5 / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": f5}
+        del a, w5
+
+        w4 = workloads.paged_decode()
+        qd, kc, vc = w4.q.cuda(), w4.k_cache.cuda(), w4.v_cache.cuda()
+        bt = torch.from_numpy(w4.block_table).cuda()
+        sl = torch.from_numpy(w4.seqlens).cuda()
+        ws = torch.empty(fa.fa_decode_paged_workspace_size(64, 32, 128, bt.shape[1], 16, 512),
+                         dtype=torch.uint8, device="cuda")
+        od = torch.empty_like(qd)
+        ld = torch.empty((64, 32), dtype=torch.float32, device="cuda")
+        nb = decode_bytes(w4)
+        ms = time_calls(lambda: fa.fa_decode_paged(qd, kc, vc, bt, sl, w4.scale, -1, 512, out=od,
+                                                   lse=ld, workspace=ws), args.steps, args.warmup)
+        gbs = nb / ms / 1e6
+        wl["paged_decode"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb,
+                              "kernels": "decode_split + decode_merge"}
+        result["roofline_decode"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                     "traffic": load_traffic("decode_paged", DECODE_SRC)}
+        del qd, kc, vc, w4
+        torch.cuda.empty_cache()
+    result["workloads"] = wl
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w2, flops2)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

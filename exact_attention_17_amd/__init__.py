@@ -1,0 +1,229 @@
+"""Python binding of the MI355X fused exact-attention library (include/fa.h).
+
+Thin ctypes marshalling only: every step of the computation runs in the HIP
+kernels of libfa.so.  The functions keep the C names:
+
+    fa_fwd(q, k, v, ...)                 dense prefill forward
+    fa_fwd_varlen(q, k, v, cu_q, cu_k, ...)  packed varlen prefill
+    fa_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, ...)
+    fa_decode_paged_workspace_size(...)
+
+Tensors are torch CUDA(HIP) tensors used purely as device memory; work is
+enqueued on torch's current stream.  There is no CPU fallback: if libfa.so is
+missing or no GPU is present the calls raise.
+"""
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from .build import LIB_PATH
+
+FA_OK = 0
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+           3: "decode workspace missing or too small", 4: "HIP kernel launch failed"}
+
+_lib = None
+
+_EXPORTS = {
+    "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fa_fwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p]
+               + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]),
+    "fa_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 2
+                      + [ctypes.c_int] * 8 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_void_p]),
+    "fa_decode_paged_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 6),
+    "fa_decode_paged": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 2
+                        + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_void_p, ctypes.c_size_t,
+                                                ctypes.c_void_p]),
+}
+
+
+class FAError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {_STATUS.get(status, 'unknown')} (status {status})")
+        self.status = status
+
+
+def load_library(path=None):
+    """Load libfa.so (built by exact_attention_17_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m exact_attention_17_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    return list(_EXPORTS)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != FA_OK:
+        raise FAError(fn, status)
+
+
+def _need(t, name, dtype=None, ndim=None, device=True):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def cu_seqlens_from_lengths(lengths):
+    """Host helper: per-sequence lengths -> cumulative offsets of length B+1
+    (lengths [100, 200, 150] -> [0, 100, 300, 450])."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    if lengths.ndim != 1 or (lengths < 0).any():
+        raise ValueError("lengths must be a 1-D array of non-negative integers")
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    if cu[-1] >= 2 ** 31:
+        raise ValueError("total length exceeds int32")
+    return cu.astype(np.int32)
+
+
+def lengths_from_cu_seqlens(cu):
+    cu = np.asarray(cu, dtype=np.int64)
+    if cu.ndim != 1 or len(cu) < 1 or cu[0] != 0 or (np.diff(cu) < 0).any():
+        raise ValueError("cu_seqlens must start at 0 and be non-decreasing")
+    return np.diff(cu).astype(np.int32)
+
+
+def fa_fwd(q, k, v, softmax_scale=None, causal=False, window=(-1, -1), out=None,
+           lse=None, return_lse=True, stream=None):
+    """Dense prefill: q (B, Lq, Hq, d), k/v (B, Lk, Hkv, d) bf16 -> O, LSE (B, Hq, Lq)."""
+    torch = _torch()
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 4)
+    B, Lq, Hq, d = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Lk, Hkv, d) or tuple(v.shape) != (B, Lk, Hkv, d):
+        raise ValueError("k and v must be (B, Lk, Hkv, d) matching q")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 4)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Lq, Lk, Hq, Hkv, d,
+                    scale, int(bool(causal)), int(window[0]), int(window[1]), _stream(stream))
+    _check("fa_fwd", st)
+    return out, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                  softmax_scale=None, causal=False, window=(-1, -1), out=None, lse=None,
+                  return_lse=True, stream=None):
+    """Packed varlen prefill: q (total_q, Hq, d), k/v (total_k, Hkv, d), cu_seqlens int32
+    device tensors of length B+1 -> O, LSE (Hq, total_q)."""
+    torch = _torch()
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 3)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    if tuple(v.shape) != (total_k, Hkv, d) or k.shape[2] != d:
+        raise ValueError("k and v must be (total_k, Hkv, d)")
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    st = lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                           _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k), total_q,
+                           total_k, Hq, Hkv, d, scale, int(bool(causal)), int(window[0]),
+                           int(window[1]), _stream(stream))
+    _check("fa_fwd_varlen", st)
+    return out, lse
+
+
+def fa_decode_paged_workspace_size(B, Hq, d, max_blocks_per_seq, page_size, split_tokens=0):
+    return int(load_library().fa_decode_paged_workspace_size(B, Hq, d, max_blocks_per_seq,
+                                                              page_size, split_tokens))
+
+
+def fa_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale=None,
+                    window_left=-1, split_tokens=0, out=None, lse=None, workspace=None,
+                    return_lse=True, stream=None):
+    """Paged decode: q (B, 1, Hq, d), caches [num_pages, page_size, Hkv, d],
+    block_table int32 [B, max_blocks], cache_seqlens int32 [B] -> O, LSE (B, Hq)."""
+    torch = _torch()
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, one, Hq, d = q.shape
+    if one != 1:
+        raise ValueError("q must be (B, 1, Hq, d)")
+    num_pages, page_size, Hkv, dk = k_cache.shape
+    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [num_pages, page_size, Hkv, d]")
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    max_blocks = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    need = fa_decode_paged_workspace_size(B, Hq, d, max_blocks, page_size, split_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib.fa_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                             _ptr(cache_seqlens), _ptr(out), _ptr(lse), B, Hq, Hkv, d, num_pages,
+                             page_size, max_blocks, scale, int(window_left), int(split_tokens),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream))
+    _check("fa_decode_paged", st)
+    return out, lse
+
+
+__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_decode_paged", "fa_decode_paged_workspace_size",
+           "load_library", "exported_symbols", "cu_seqlens_from_lengths",
+           "lengths_from_cu_seqlens", "FAError", "LIB_PATH"]

@@ -1,0 +1,345 @@
+// Split-KV flash-decoding over a paged KV cache for gfx950.
+//
+// What it computes (cited by page title and section):
+//   one query row per request attends to that request's cached keys, read in
+//   place from fixed-size pages through a block table, without copying them
+//   into a contiguous tensor ("FIA / FlashAttention" explainer, sec. 2;
+//   configuration skill page, appendix on PagedAttention).  Because one query
+//   row per (request, head) gives too little parallelism, the keys are also
+//   split along the sequence: several workgroups take different key ranges of
+//   the same head and a final reduction merges their partial results (skill
+//   page appendix, FlashDecoding / Split-KV).  The merge is the online-softmax
+//   reduction by log-sum-exp (explainer, sec. 2).  All query heads of a GQA
+//   group are served by one read of their KV head (explainer, sec. 2,
+//   head-query fusion; skill page GQA appendix).
+//
+// Mapping onto CDNA4 (our design):
+//   * decode_split: one workgroup (4 wave64s) per (request, KV head, split of
+//     split_tokens keys).  Each wave takes 64-key chunks of the split.
+//     Scores for the group's query heads come from v_mfma_f32_16x16x32_bf16
+//     with the (zero-padded) query heads as the 16-row A operand and K rows
+//     as the B operand, loaded straight from the cache in MFMA layout (each
+//     lane reads 16 contiguous bytes of one key row).  P goes through a small
+//     per-wave LDS buffer; P*V runs on the fp32 VALU with V read in fully
+//     coalesced 256-byte rows.  The four waves merge in LDS and write one
+//     partial (O_s normalised, LSE_s) per query head.
+//   * decode_merge: one workgroup per (request, query head) combines the
+//     partials by their LSE and writes bf16 O and fp32 LSE.
+//   * Keys at or past a request's length (and before its window) never reach
+//     the result: they read a safe in-bounds cache row (never an unused
+//     block-table entry), their scores are set to -inf and their V rows to
+//     zero, so NaN or stale cache contents cannot leak in.  When page_size is
+//     a multiple of 16 the page id of each 16-key block is wave-uniform and
+//     comes from one scalar load.
+#include "fa_internal.h"
+#include "gfx950.h"
+
+#include <math.h>
+
+namespace fa {
+
+namespace {
+constexpr float kRescaleTau = 8.0f;
+constexpr float kLn2 = 0.6931471805599453f;
+}  // namespace
+
+// GR = padded number of query heads handled per workgroup (1, 2, 4 or 8).
+// PAGE16: page_size is a multiple of 16, so every 16-key block lies in one page.
+template <int D, int GR, bool PAGE16>
+__global__ __launch_bounds__(kDecodeThreads, 2)
+void decode_split_kernel(DecodeParams p) {
+  constexpr int KT = D / 32;              // MFMA k-steps over d
+  constexpr int VCH = D / 8;              // 16-byte chunks per V row
+  constexpr int VKEYS = 64 / VCH;         // keys covered by one V load instruction
+  constexpr int VLOADS = kDecodeChunk / VKEYS;
+  constexpr int PST = GR < 4 ? 4 : GR;    // P row stride in the LDS buffer (floats)
+
+  __shared__ __attribute__((aligned(16))) float p_lds[4][kDecodeChunk][PST];
+  __shared__ float a_lds[4][16];
+  __shared__ float m_lds[4][GR], l_lds[4][GR];
+  __shared__ __attribute__((aligned(16))) float o_lds[4][GR][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = blockIdx.x, b = blockIdx.z;
+  const int kvh = blockIdx.y / p.sub_groups, sub = blockIdx.y % p.sub_groups;
+  const int h0 = kvh * p.group + sub * GR;
+  const int nrow = min(GR, p.group - sub * GR);
+
+  const int len = p.seqlens[b];
+  const int lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
+  const int split_base = s * p.split_tokens;
+  const int k_beg = max(split_base, lo);
+  const int k_end = min(len, split_base + p.split_tokens);
+  if (k_beg >= k_end) return;
+
+  const int* bt = p.block_table + (int64_t)b * p.max_blocks;
+  const int64_t tok_stride = (int64_t)p.Hkv * D;    // elements between cache slots
+  const uint16_t* kcache = p.k_cache + (int64_t)kvh * D;
+  const uint16_t* vcache = p.v_cache + (int64_t)kvh * D;
+
+  // Q heads as the A operand: lane row i = lane % 16, d = 32t + 8*(lane/16) + 0..7
+  const int qi = lane & 15, qg = lane >> 4;
+  u32x4 qa[KT];
+  {
+    const bool ok = qi < nrow;
+    const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + h0 + qi) * D + 8 * qg;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      qa[t] = ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * t) : u32x4{0, 0, 0, 0};
+  }
+
+  // S layout: lane (key n = lane%16, row group g = lane/16) holds rows 4g..4g+3.
+  const int sn = lane & 15, sg = lane >> 4;
+  float m_ref[4], l_part[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { m_ref[r] = -INFINITY; l_part[r] = 0.f; }
+  // PV layout: lane (key j = lane / VCH, d chunk vc = lane % VCH)
+  const int vj = lane / VCH, vc = lane % VCH;
+  float oacc[GR][8];
+#pragma unroll
+  for (int r = 0; r < GR; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oacc[r][e] = 0.f;
+
+  const float c = p.scale_log2;
+  const int nchunks = (k_end - split_base + kDecodeChunk - 1) / kDecodeChunk;
+  const int c0 = (k_beg - split_base) / kDecodeChunk;
+
+  for (int ch = c0 + wave; ch < nchunks; ch += 4) {
+    const int kc = split_base + ch * kDecodeChunk;
+    // ---- loads: K in MFMA B layout, V in coalesced rows -------------------
+    // Keys outside [k_beg, k_end) read a safe in-bounds row (page 0 when their
+    // page is not in use); their scores are masked and their V rows zeroed.
+    const bool partial = kc < k_beg || kc + kDecodeChunk > k_end;   // wave-uniform
+    int pid16[4];
+    if (PAGE16) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int key0 = kc + 16 * blk;
+        pid16[blk] = key0 < k_end ? __builtin_amdgcn_readfirstlane(bt[key0 / p.page_size]) : 0;
+      }
+    }
+    auto row_of = [&](int key, int blk) -> int64_t {   // cache slot index of a key
+      if (PAGE16) return (int64_t)pid16[blk] * p.page_size + key % p.page_size;
+      const bool ok = key >= 0 && key < k_end;
+      const int pid = ok ? bt[key / p.page_size] : 0;
+      return (int64_t)pid * p.page_size + (ok ? key % p.page_size : 0);
+    };
+    u32x4 kr[4][KT];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const uint16_t* src = kcache + row_of(kc + 16 * blk + sn, blk) * tok_stride + 8 * sg;
+#pragma unroll
+      for (int t = 0; t < KT; ++t) kr[blk][t] = *reinterpret_cast<const u32x4*>(src + 32 * t);
+    }
+    u32x4 vr[VLOADS];
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int key = kc + VKEYS * i + vj;
+      const uint16_t* src = vcache + row_of(key, (VKEYS * i) / 16) * tok_stride + 8 * vc;
+      vr[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i) {
+        const int key = kc + VKEYS * i + vj;
+        if (!(key >= k_beg && key < k_end)) vr[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    // ---- scores S = Q K^T (rows = query heads, columns = 16 keys per block)
+    f32x4 sacc[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      sacc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < KT; ++t) sacc[blk] = mfma16x16x32(qa[t], kr[blk][t], sacc[blk]);
+      const int key = kc + 16 * blk + sn;
+      if (partial && !(key >= k_beg && key < k_end))
+        sacc[blk] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+    // ---- online softmax per query row ------------------------------------
+    bool any_up = false;
+    float tmax[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float mx = fmaxf(fmaxf(sacc[0][r], sacc[1][r]), fmaxf(sacc[2][r], sacc[3][r]));
+      tmax[r] = row16_max(mx) * c;
+      any_up |= tmax[r] > m_ref[r] + kRescaleTau;
+    }
+    if (wave_any(any_up)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool up = tmax[r] > m_ref[r] + kRescaleTau;
+        const float m_new = up ? tmax[r] : m_ref[r];
+        const float alpha = up ? exp2_fast(m_ref[r] - m_new) : 1.f;
+        l_part[r] *= alpha;
+        m_ref[r] = m_new;
+        if (sn == 0 && 4 * sg + r < 16) a_lds[wave][4 * sg + r] = alpha;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < GR; ++r) {
+        const float alpha = a_lds[wave][r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[r][e] *= alpha;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mb = m_ref[r] == -INFINITY ? 0.f : m_ref[r];
+        pv[r] = exp2_fast(fmaf(sacc[blk][r], c, -mb));
+        l_part[r] += pv[r];
+      }
+      if (4 * sg < GR) {
+        float* dst = &p_lds[wave][16 * blk + sn][4 * sg];
+        if (GR >= 4) {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < GR; ++r) dst[r] = pv[r];
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---- O += P V on the VALU (fp32) -------------------------------------
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int kl = VKEYS * i + vj;
+      float pr[GR];
+      if (GR >= 4) {
+#pragma unroll
+        for (int r4 = 0; r4 < GR; r4 += 4) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(&p_lds[wave][kl][r4]);
+          pr[r4] = t4[0]; pr[r4 + 1] = t4[1]; pr[r4 + 2] = t4[2]; pr[r4 + 3] = t4[3];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < GR; ++r) pr[r] = p_lds[wave][kl][r];
+      }
+      float vf[8];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        vf[2 * e2] = bf16lo(vr[i][e2]);
+        vf[2 * e2 + 1] = bf16hi(vr[i][e2]);
+      }
+#pragma unroll
+      for (int r = 0; r < GR; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[r][e] = fmaf(pr[r], vf[e], oacc[r][e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- per-wave totals: l over the 16 key lanes, O over the key groups -----
+#pragma unroll
+  for (int r = 0; r < 4; ++r) l_part[r] = row16_sum(l_part[r]);
+#pragma unroll
+  for (int r = 0; r < GR; ++r) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = oacc[r][e];
+#pragma unroll
+      for (int off = VCH; off < 64; off <<= 1)
+        x += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(x)));
+      oacc[r][e] = x;
+    }
+  }
+  if (sn == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (4 * sg + r < GR) {
+        m_lds[wave][4 * sg + r] = m_ref[r];
+        l_lds[wave][4 * sg + r] = l_part[r];
+      }
+    }
+  }
+  if (vj == 0) {
+#pragma unroll
+    for (int r = 0; r < GR; ++r) {
+      *reinterpret_cast<f32x4*>(&o_lds[wave][r][8 * vc]) =
+          f32x4{oacc[r][0], oacc[r][1], oacc[r][2], oacc[r][3]};
+      *reinterpret_cast<f32x4*>(&o_lds[wave][r][8 * vc + 4]) =
+          f32x4{oacc[r][4], oacc[r][5], oacc[r][6], oacc[r][7]};
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the four waves; write the split's partial -------------------
+  for (int idx = tid; idx < GR * D; idx += kDecodeThreads) {
+    const int r = idx / D, d = idx % D;
+    if (r >= nrow) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, m_lds[w][r]);
+    float lsum = 0.f, osum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = m_lds[w][r] == -INFINITY ? 0.f : exp2_fast(m_lds[w][r] - M);
+      lsum += f * l_lds[w][r];
+      osum += f * o_lds[w][r][d];
+    }
+    const int64_t slot = ((int64_t)b * p.Hq + h0 + r) * p.max_splits + s;
+    p.part_o[slot * D + d] = osum / lsum;
+    if (d == 0) p.part_lse[slot] = M + log2_fast(lsum);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(128)
+void decode_merge_kernel(DecodeParams p) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int len = p.seqlens[b];
+  const int lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
+  const int s_beg = lo / p.split_tokens;
+  const int s_end = (len + p.split_tokens - 1) / p.split_tokens;
+  const int64_t row = (int64_t)b * p.Hq + h;
+  const float* plse = p.part_lse + row * p.max_splits;
+  const float* po = p.part_o + row * p.max_splits * D;
+
+  float M = -INFINITY;
+  for (int s = s_beg; s < s_end; ++s) M = fmaxf(M, plse[s]);
+  float wsum = 0.f, acc = 0.f;
+  for (int s = s_beg; s < s_end; ++s) {
+    const float wgt = exp2_fast(plse[s] - M);
+    wsum += wgt;
+    if (tid < D) acc += wgt * po[(int64_t)s * D + tid];
+  }
+  const bool empty = s_end <= s_beg;
+  if (tid < D) {
+    const float out = empty ? 0.f : acc / wsum;
+    p.o[row * D + tid] = (uint16_t)(pack_bf16x2(out, 0.f) & 0xffffu);
+  }
+  if (p.lse && tid == 0) p.lse[row] = empty ? -INFINITY : (M + log2_fast(wsum)) * kLn2;
+}
+
+template <int D, bool PAGE16>
+static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
+  const dim3 grid(p.max_splits, p.Hkv * p.sub_groups, p.B), block(kDecodeThreads);
+  switch (rows) {
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, PAGE16>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, PAGE16>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4, PAGE16>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, 8, PAGE16>), grid, block, 0, stream, p); break;
+  }
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeParams& p, int rows, hipStream_t stream) {
+  if (p.page_size % 16 == 0) launch_split<D, true>(p, rows, stream);
+  else launch_split<D, false>(p, rows, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid2(p.Hq, p.B), block2(128);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), grid2, block2, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeParams& p, int d, int rows, hipStream_t stream) {
+  return d == 128 ? launch_decode_d<128>(p, rows, stream) : launch_decode_d<64>(p, rows, stream);
+}
+
+}  // namespace fa

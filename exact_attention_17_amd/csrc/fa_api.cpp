@@ -1,0 +1,202 @@
+// C-ABI entry points: argument validation, planning and kernel dispatch.
+// Every check runs on the host before any HIP call; a failed check returns a
+// status and enqueues nothing.
+#include "fa.h"
+#include "fa_internal.h"
+
+#include <math.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+constexpr int64_t kMaxBatchElems = (int64_t)1 << 30;   // bf16 elements: < 2^31 bytes
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fa_status check_common(int Hq, int Hkv, int d, float scale, int causal, int wl, int wr) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (d < 1) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (wl < -1 || wr < -1) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+fa_status check_tensors(const void* q, const void* k, const void* v, const void* o, const float* lse) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+// XCD-aware mapping needs the KV-group count to split evenly over 8 XCDs.
+int xcd_groups(int kv_groups) { return (kv_groups > 0 && kv_groups % 8 == 0) ? kv_groups : 0; }
+
+int pow2_rows(int g) {
+  int r = 1;
+  while (r < g && r < 8) r <<= 1;
+  return r;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128)";
+    case FA_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Lq, int Lk, int Hq, int Hkv, int d,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 void* stream) {
+  fa_status st = check_common(Hq, Hkv, d, softmax_scale, causal, window_left, window_right);
+  if (st != FA_OK) return st;
+  if ((st = check_tensors(q, k, v, o, lse)) != FA_OK) return st;
+  if (B < 1 || Lq < 1 || Lk < 1) return FA_ERR_INVALID_ARG;
+  // per-batch tensors are addressed with 32-bit byte offsets
+  if ((int64_t)Lq * Hq * d >= kMaxBatchElems || (int64_t)Lk * Hkv * d >= kMaxBatchElems)
+    return FA_ERR_INVALID_ARG;
+
+  fa::PrefillParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B; p.Lq = Lq; p.Lk = Lk;
+  p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.q_tok_stride = (int64_t)Hq * d;
+  p.k_tok_stride = (int64_t)Hkv * d;
+  p.q_batch_stride = (int64_t)Lq * Hq * d;
+  p.k_batch_stride = (int64_t)Lk * Hkv * d;
+  p.lse_seq_stride = Lq;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
+  p.xcd_groups = xcd_groups(B * Hkv);
+  if ((int64_t)p.num_q_tiles * B * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
+  hipError_t e = fa::launch_prefill(p, d, false, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                        int Hq, int Hkv, int d, float softmax_scale, int causal,
+                        int window_left, int window_right, void* stream) {
+  fa_status st = check_common(Hq, Hkv, d, softmax_scale, causal, window_left, window_right);
+  if (st != FA_OK) return st;
+  if ((st = check_tensors(q, k, v, o, lse)) != FA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return FA_ERR_INVALID_ARG;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FA_ERR_INVALID_ARG;
+  if (total_q > 0 && max_seqlen_q < 1) return FA_ERR_INVALID_ARG;
+  if ((int64_t)total_q * Hq * d >= kMaxBatchElems || (int64_t)total_k * Hkv * d >= kMaxBatchElems)
+    return FA_ERR_INVALID_ARG;
+  if (total_q == 0) return FA_OK;
+
+  fa::PrefillParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.B = B; p.Lq = max_seqlen_q; p.Lk = max_seqlen_k;
+  p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.q_tok_stride = (int64_t)Hq * d;
+  p.k_tok_stride = (int64_t)Hkv * d;
+  p.lse_seq_stride = total_q;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  // tile slots: sequence b owns [cu_q[b]/128 + b, cu_q[b+1]/128 + b + 1)
+  p.num_q_tiles = total_q / fa::kBlockM + B;
+  p.xcd_groups = xcd_groups(Hkv);
+  if ((int64_t)p.num_q_tiles * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
+  hipError_t e = fa::launch_prefill(p, d, true, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+static int effective_split(int split_tokens) { return split_tokens == 0 ? fa::kDefaultSplit : split_tokens; }
+
+static bool decode_sizes_ok(int B, int Hq, int d, int max_blocks, int page_size, int split_tokens) {
+  if (B < 1 || Hq < 1 || max_blocks < 1 || page_size < 1) return false;
+  if (d != 64 && d != 128) return false;
+  if (split_tokens < 0 || split_tokens % 16 != 0) return false;
+  if ((int64_t)max_blocks * page_size >= kMaxElems) return false;
+  return true;
+}
+
+static size_t part_o_bytes(int B, int Hq, int d, int max_splits) {
+  const size_t n = (size_t)B * Hq * max_splits * d * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_blocks_per_seq,
+                                      int page_size, int split_tokens) {
+  if (!decode_sizes_ok(B, Hq, d, max_blocks_per_seq, page_size, split_tokens)) return 0;
+  const int split = effective_split(split_tokens);
+  const int max_splits = (int)cdiv((int64_t)max_blocks_per_seq * page_size, split);
+  const size_t lse_bytes = ((size_t)B * Hq * max_splits * sizeof(float) + 255) & ~(size_t)255;
+  return part_o_bytes(B, Hq, d, max_splits) + lse_bytes;
+}
+
+fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                          const int* block_table, const int* cache_seqlens,
+                          void* o, float* lse, int B, int Hq, int Hkv, int d,
+                          int num_pages, int page_size, int max_blocks_per_seq,
+                          float softmax_scale, int window_left, int split_tokens,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status st = check_common(Hq, Hkv, d, softmax_scale, 0, window_left, -1);
+  if (st != FA_OK) return st;
+  if ((st = check_tensors(q, k_cache, v_cache, o, lse)) != FA_OK) return st;
+  if (!block_table || !cache_seqlens || !aligned(block_table, 4) || !aligned(cache_seqlens, 4))
+    return FA_ERR_INVALID_ARG;
+  if (num_pages < 1) return FA_ERR_INVALID_ARG;
+  if (!decode_sizes_ok(B, Hq, d, max_blocks_per_seq, page_size, split_tokens)) return FA_ERR_INVALID_ARG;
+  if (B > 65535 || (int64_t)Hkv * cdiv(Hq / Hkv, pow2_rows(Hq / Hkv)) > 65535) return FA_ERR_INVALID_ARG;
+  if ((int64_t)num_pages * page_size * Hkv * d >= ((int64_t)1 << 40)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_decode_paged_workspace_size(B, Hq, d, max_blocks_per_seq, page_size, split_tokens);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+
+  const int split = effective_split(split_tokens);
+  fa::DecodeParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const uint16_t*>(k_cache);
+  p.v_cache = static_cast<const uint16_t*>(v_cache);
+  p.block_table = block_table;
+  p.seqlens = cache_seqlens;
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  const int rows = pow2_rows(p.group);
+  p.sub_groups = (int)cdiv(p.group, rows);
+  p.page_size = page_size;
+  p.max_blocks = max_blocks_per_seq;
+  p.split_tokens = split;
+  p.max_splits = (int)cdiv((int64_t)max_blocks_per_seq * page_size, split);
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_o_bytes(B, Hq, d, p.max_splits));
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.win_left = window_left;
+  hipError_t e = fa::launch_decode(p, d, rows, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

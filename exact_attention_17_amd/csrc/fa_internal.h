@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI layer (fa_api.cpp) and the HIP kernels.
+// Everything here is validated by the caller before a launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Prefill tile shape: one workgroup = 4 waves = 128 query rows (32 per wave),
+// iterating over 64-key tiles.
+constexpr int kPrefillThreads = 256;
+constexpr int kBlockM = 128;
+constexpr int kBlockN = 64;
+
+// Decode split kernel: one workgroup = 4 waves per (request, KV head, split).
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeChunk = 64;     // keys per wave iteration
+constexpr int kDefaultSplit = 512;
+
+struct PrefillParams {
+  const uint16_t* q;       // bf16 bits
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;              // may be null
+  const int* cu_q;         // varlen only
+  const int* cu_k;
+  int B, Lq, Lk;           // dense: lengths; varlen: Lq/Lk unused
+  int Hq, Hkv, group;      // group = Hq / Hkv
+  int64_t q_tok_stride;    // elements between consecutive tokens = H*d
+  int64_t k_tok_stride;
+  int64_t q_batch_stride;  // dense only: Lq*Hq*d
+  int64_t k_batch_stride;  // dense only: Lk*Hkv*d
+  int lse_seq_stride;      // dense: Lq (lse is (B, Hq, Lq)); varlen: total_q
+  float scale_log2;        // softmax_scale * log2(e)
+  int causal, win_left, win_right;
+  int num_q_tiles;         // dense: ceil(Lq / kBlockM); varlen: total tile slots
+  int xcd_groups;          // >0: XCD-aware work mapping with this many KV groups
+};
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int* block_table;
+  const int* seqlens;
+  uint16_t* o;
+  float* lse;              // may be null
+  float* part_o;           // [B][Hq][max_splits][d]
+  float* part_lse;         // [B][Hq][max_splits]  (log2 units)
+  int B, Hq, Hkv, group, sub_groups;
+  int page_size, max_blocks, split_tokens, max_splits;
+  float scale_log2;
+  int win_left;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int d, bool varlen, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int d, int rows, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,98 @@
+// Device helpers for CDNA4 / gfx950: MFMA wrappers, bf16 packing, wave64
+// cross-lane reductions and the base-2 exponential.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_DEV __device__ __forceinline__
+
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16).  Lane l holds row/column
+// l % 32 of A/B and 8 consecutive contraction elements chosen by l / 32; the
+// accumulator holds column l % 32 and rows 8*(r/4) + 4*(l/32) + r%4, r < 16.
+FA_DEV f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).  Lane l holds row/column
+// l % 16 and 8 contraction elements chosen by l / 16; the accumulator holds
+// column l % 16 and rows 4*(l/16) + r, r < 4.
+FA_DEV f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round-to-nearest-even
+// (one v_cvt_pk_bf16_f32 on gfx950).
+FA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+FA_DEV float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+FA_DEV float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+FA_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+FA_DEV float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value from lane (lane ^ 32): swaps the two halves of a wave64.
+FA_DEV float xor32(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ 32) << 2,
+                                                     __float_as_int(x)));
+}
+
+// Butterfly max / sum over the 16 lanes of a DPP row (lanes 16k..16k+15).
+// row_ror rotates within the row, quad_perm swaps within 4-lane groups.
+template <int CTRL>
+FA_DEV float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppQuadXor2 = 0x4e;   // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor1 = 0xb1;   // quad_perm [1,0,3,2]
+
+FA_DEV float row16_max(float x) {
+  x = fmaxf(x, dpp<kDppRowRor8>(x));
+  x = fmaxf(x, dpp<kDppRowRor4>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  return x;
+}
+
+FA_DEV float row16_sum(float x) {
+  x += dpp<kDppRowRor8>(x);
+  x += dpp<kDppRowRor4>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppQuadXor1>(x);
+  return x;
+}
+
+FA_DEV bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Raw buffer resource over [base, base + bytes).  A load whose byte offset is
+// at or past `bytes` returns zeros, so ragged tiles need no branches; offsets
+// of invalid rows are set to kOob (bytes must stay below 2^31).
+constexpr uint32_t kOob = 0x80000000u;
+FA_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+FA_DEV u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+}  // namespace fa

@@ -1,0 +1,138 @@
+/*
+ * fa.h -- C ABI of an MI355X (gfx950) library for fused exact attention.
+ *
+ * The library computes O = softmax(scale * Q K^T + mask) V together with the
+ * per-row log-sum-exp, tile by tile with an online softmax, so the score
+ * matrix never reaches device memory.  Sources, cited by page title and
+ * section:
+ *   - "FlashAttention-3 vs naive attention: inference comparison (FA3)",
+ *     sec. 1.1 (the definition), 1.2 (no materialised S or P), 2.1/2.2
+ *     (prefill vs decode), 4.2 (one fused kernel);
+ *   - "FIA / FlashAttention" explainer, sec. 1 (tiling, online softmax with a
+ *     running max m and normaliser l) and sec. 2 (flash-decoding with an
+ *     online-softmax reduction over a paged KV cache);
+ *   - "flash-attention" configuration skill page, sec. 3.1-3.5 and the
+ *     appendix (argument names and shapes, causal, window_size, cu_seqlens,
+ *     block_table, split-KV, GQA broadcast).
+ *
+ * Conventions shared by every entry point
+ *   - Element type of q, k, v, o, caches: bfloat16, row-major, contiguous,
+ *     last dimension (head_dim) has stride 1.  lse: float32, natural log.
+ *   - All pointers except `stream` are DEVICE pointers owned by the caller;
+ *     the library never allocates, frees, synchronises or keeps a pointer
+ *     after the call returns.  q/k/v/o/cache pointers must be 16-byte
+ *     aligned.  `lse` may be NULL (then no LSE is written).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns at once.
+ *   - head_dim d is 64 or 128.  Hkv must divide Hq; query head h reads KV head
+ *     h / (Hq / Hkv) (GQA/MQA broadcast with no copy of K/V).
+ *   - softmax_scale must be finite and > 0 (callers use 1/sqrt(d) by default).
+ *   - Masking: causal attention is aligned bottom-right, i.e. query row i of a
+ *     sequence with Lq queries and Lk keys sits at key position i + Lk - Lq
+ *     and sees keys j <= i + Lk - Lq.  window_left / window_right >= 0 limit
+ *     the keys to [i + Lk - Lq - left, i + Lk - Lq + right] inclusive;
+ *     -1 leaves that side unbounded.  A row with no visible key gets O = 0
+ *     and LSE = -inf.
+ *   - Errors: every argument is validated on the host before any HIP call.
+ *     On a non-zero status nothing has been enqueued and no output has been
+ *     touched.  FA_ERR_HIP reports a failed kernel launch.  Device-side
+ *     preconditions that cannot be checked without reading device memory
+ *     (monotone cu_seqlens ending at total, block_table entries in
+ *     [0, num_pages) for the pages a request uses, cache_seqlens[b] <=
+ *     max_blocks_per_seq * page_size) are the caller's responsibility.
+ *   - Calls are reentrant and thread-safe: the library has no global state.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or flag      */
+  FA_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim not in {64,128}  */
+  FA_ERR_WORKSPACE = 3,     /* decode workspace missing or too small          */
+  FA_ERR_HIP = 4            /* a HIP launch failed                            */
+} fa_status;
+
+/* Static English text for a status code.  Never NULL. */
+const char* fa_status_string(fa_status status);
+
+/*
+ * Dense prefill forward (skill page sec. 3.1/3.2, flash_attn_func;
+ * "FlashAttention-3 vs naive attention" sec. 2.1).
+ *   q, o : (B, Lq, Hq, d)      k, v : (B, Lk, Hkv, d)
+ *   lse  : (B, Hq, Lq) float32, or NULL
+ * B, Lq, Lk >= 1 (B*Hq*Lq and B*Hkv*Lk*d must fit in 2^31).  causal is 0/1.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Lq, int Lk, int Hq, int Hkv, int d,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 void* stream);
+
+/*
+ * Packed variable-length prefill (skill page sec. 3.4 and the appendix on
+ * continuous batching, flash_attn_varlen_func): sequences are concatenated
+ * with no padding and never attend across each other.
+ *   q, o : (total_q, Hq, d)    k, v : (total_k, Hkv, d)
+ *   cu_seqlens_q, cu_seqlens_k : device int32 arrays of B+1 cumulative
+ *       offsets, cu[0] = 0, cu[B] = total (e.g. lengths [100,200,150] give
+ *       [0,100,300,450]);
+ *   max_seqlen_q / max_seqlen_k : host upper bounds of the per-sequence
+ *       lengths (only used for validation and planning);
+ *   lse  : (Hq, total_q) float32, or NULL.
+ * Masks apply per sequence with that sequence's own Lq_b and Lk_b.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                        int Hq, int Hkv, int d, float softmax_scale, int causal,
+                        int window_left, int window_right, void* stream);
+
+/*
+ * Bytes of device workspace fa_decode_paged needs for these sizes (split
+ * partials: one float32 row of d values plus one float32 LSE per request,
+ * query head and split).  split_tokens = 0 selects the default of 512.
+ * Returns 0 if the sizes are invalid.
+ */
+size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_blocks_per_seq,
+                                      int page_size, int split_tokens);
+
+/*
+ * One decode step over a paged KV cache with split-KV flash-decoding
+ * (skill page appendix: PagedAttention, FlashDecoding / Split-KV;
+ * "FIA / FlashAttention" explainer sec. 2).  Each request's one query row
+ * attends to its cache_seqlens[b] cached tokens; the keys are cut into
+ * chunks of split_tokens, each chunk yields a partial (LSE, O) and a second
+ * kernel merges the partials by their log-sum-exp.
+ *   q, o     : (B, 1, Hq, d)
+ *   k_cache, v_cache : [num_pages, page_size, Hkv, d]
+ *   block_table : device int32 [B, max_blocks_per_seq]; token j of request b
+ *       is in page block_table[b][j / page_size], slot j % page_size.  Only
+ *       the first ceil(cache_seqlens[b] / page_size) entries of a row are read.
+ *   cache_seqlens : device int32 [B], 0 <= len <= max_blocks_per_seq*page_size.
+ *       A request with len 0 gets O = 0, LSE = -inf.
+ *   lse      : (B, Hq) float32, or NULL
+ *   window_left : -1 for none, else only the last window_left + 1 tokens count.
+ *   split_tokens : 0 (= 512) or a positive multiple of 16.
+ *   workspace : device buffer of at least fa_decode_paged_workspace_size(...)
+ *       bytes, 256-byte aligned; its contents on entry do not matter.
+ * Cache contents of unused pages and of slots at or past a request's length
+ * never influence the result (they may hold NaN).
+ */
+fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                          const int* block_table, const int* cache_seqlens,
+                          void* o, float* lse, int B, int Hq, int Hkv, int d,
+                          int num_pages, int page_size, int max_blocks_per_seq,
+                          float softmax_scale, int window_left, int split_tokens,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

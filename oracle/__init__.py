@@ -29,6 +29,9 @@ Readings where the pages are silent (each listed in the design doc):
   natural-log log-sum-exp of the scaled scores; a row with no visible key has
   O = 0 and LSE = -inf.
 
+Inputs are numpy arrays; a uint16 array is taken as bfloat16 bit patterns
+(numpy has no bfloat16 type) and converted exactly to float64.
+
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 closed forms, invariants, a pure-Python brute force and PyTorch's CPU
 ``scaled_dot_product_attention`` in float64.  No function is parity-unpinned.

@@ -13,7 +13,12 @@ import numpy as np
 
 
 def _f64(x):
-    return np.asarray(x, dtype=np.float64)
+    """Inputs as float64.  numpy has no bfloat16, so a uint16 array is read as
+    bfloat16 bit patterns (exact: bf16 is the top half of an fp32)."""
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
 
 
 def key_visibility(Lq, Lk, causal, window_left=-1, window_right=-1, rows=None):
@@ -172,7 +177,7 @@ def decode_paged_ref(q, k_cache, v_cache, block_table, cache_seqlens, page_size,
     """
     q = _f64(q)
     B, _, Hq, d = q.shape
-    O = np.zeros((B, 1, Hq, d))
+    O = np.zeros((B, 1, Hq, d))   # caches may stay uint16 bf16 bits: only used rows convert
     LSE = np.zeros((B, Hq))
     for b in range(B):
         n = int(cache_seqlens[b])

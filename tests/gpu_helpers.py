@@ -1,0 +1,44 @@
+"""Shared helpers for the GPU tests (not collected as tests).
+
+Comparison rule, fixed for every GPU test: with O_ref the unrounded float64
+oracle output, |O - O_ref| <= 4e-3 + 1e-2 * |O_ref| element-wise for the bf16
+output, and |LSE - LSE_ref| <= 1e-4 (absolute) for the fp32 log-sum-exp; rows
+with no visible key must give O = 0 and LSE = -inf exactly.
+"""
+
+import numpy as np
+import torch
+
+O_ATOL, O_RTOL, LSE_TOL = 4e-3, 1e-2, 1e-4
+
+
+def bits(t):
+    """CPU bf16 tensor -> numpy uint16 bit patterns (the oracle reads these exactly)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def dev(t):
+    return t.to("cuda", non_blocking=False)
+
+
+def check(name, o, lse, o_ref, lse_ref):
+    """Assert the tolerance; returns (max err/tol for O, max |dLSE|)."""
+    o = f64(o) if isinstance(o, torch.Tensor) else o
+    assert o.shape == o_ref.shape, (name, o.shape, o_ref.shape)
+    assert np.isfinite(o).all(), f"{name}: non-finite output"
+    ratio = float((np.abs(o - o_ref) / (O_ATOL + O_RTOL * np.abs(o_ref))).max()) if o.size else 0.0
+    dl = 0.0
+    if lse is not None:
+        lse = f64(lse) if isinstance(lse, torch.Tensor) else lse
+        assert lse.shape == lse_ref.shape, (name, lse.shape, lse_ref.shape)
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isneginf(lse), ~fin), f"{name}: -inf LSE pattern differs"
+        dl = float(np.abs(lse[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+    print(f"[parity] {name}: max err/tol {ratio:.3f}, max |dLSE| {dl:.2e}", flush=True)
+    assert ratio <= 1.0, f"{name}: O error {ratio:.3f} x tolerance"
+    assert dl <= LSE_TOL, f"{name}: LSE error {dl:.3e}"
+    return ratio, dl

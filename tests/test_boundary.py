@@ -1,0 +1,170 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+entry point include/fa.h declares, and rejects each invalid argument with its
+status code before any HIP call (so nothing is enqueued)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import exact_attention_17_amd as fa
+from exact_attention_17_amd import build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+P = 0x10000          # a fake, 256-byte-aligned "device" address: never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB_PATH):
+        build.build_library()
+    return fa.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == sorted(["fa_status_string", "fa_fwd", "fa_fwd_varlen",
+                            "fa_decode_paged_workspace_size", "fa_decode_paged"])
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(fa.exported_symbols()) == names
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.fa_status_string(code)
+    assert lib.fa_status_string(99) == b"unknown status"
+
+
+def fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Lq=128, Lk=128, Hq=2, Hkv=1, d=64,
+             scale=0.125, causal=0, wl=-1, wr=-1)
+    a.update(kw)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Lq"], a["Lk"], a["Hq"],
+                      a["Hkv"], a["d"], a["scale"], a["causal"], a["wl"], a["wr"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(k=P + 8), INVALID),
+    (dict(lse=P + 2), INVALID), (dict(B=0), INVALID), (dict(Lq=0), INVALID), (dict(Lk=-1), INVALID),
+    (dict(Hq=3, Hkv=2), INVALID), (dict(Hkv=0), INVALID), (dict(d=0), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(scale=0.0), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(causal=2), INVALID), (dict(wl=-2), INVALID), (dict(wr=-5), INVALID),
+    (dict(Lq=1 << 20, Hq=64, d=128), INVALID),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def varlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, cq=P, ck=P, B=2, mq=10, mk=10, tq=16, tk=16, Hq=4, Hkv=2,
+             d=128, scale=0.1, causal=1, wl=-1, wr=-1)
+    a.update(kw)
+    return lib.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"], a["mq"],
+                             a["mk"], a["tq"], a["tk"], a["Hq"], a["Hkv"], a["d"], a["scale"],
+                             a["causal"], a["wl"], a["wr"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cq=None), INVALID), (dict(ck=P + 2), INVALID), (dict(B=0), INVALID),
+    (dict(tq=-1), INVALID), (dict(mq=20), INVALID), (dict(mq=0), INVALID), (dict(mk=-1), INVALID),
+    (dict(d=80), UNSUPPORTED), (dict(Hq=5), INVALID),
+])
+def test_varlen_rejects(lib, kw, code):
+    assert varlen(lib, **kw) == code
+
+
+def test_varlen_empty_batch_is_a_no_op(lib):
+    assert varlen(lib, tq=0, mq=0) == OK
+
+
+def test_workspace_size(lib):
+    ws = lib.fa_decode_paged_workspace_size
+    # 64 requests, 32 heads, d 128, 512 blocks of 16 tokens, 512-token splits -> 16 splits
+    n_o = 64 * 32 * 16 * 128 * 4
+    n_l = 64 * 32 * 16 * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert ws(64, 32, 128, 512, 16, 512) == up(n_o) + up(n_l)
+    assert ws(64, 32, 128, 512, 16, 0) == ws(64, 32, 128, 512, 16, 512)
+    assert ws(1, 1, 64, 1, 1, 16) == up(64 * 4) + up(4)
+    for bad in [(0, 32, 128, 512, 16, 0), (1, 32, 96, 4, 16, 0), (1, 32, 128, 4, 16, 24),
+                (1, 32, 128, 0, 16, 0), (1, 32, 128, 4, 0, 0), (1, 32, 128, 4, 16, -16)]:
+        assert ws(*bad) == 0
+
+
+def decode(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, bt=P, sl=P, o=P, lse=P, B=4, Hq=8, Hkv=2, d=128, pages=64, ps=16,
+             mb=8, scale=0.1, wl=-1, split=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.fa_decode_paged(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["o"], a["lse"], a["B"],
+                               a["Hq"], a["Hkv"], a["d"], a["pages"], a["ps"], a["mb"], a["scale"],
+                               a["wl"], a["split"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), INVALID), (dict(sl=P + 1), INVALID), (dict(kc=None), INVALID),
+    (dict(pages=0), INVALID), (dict(ps=0), INVALID), (dict(mb=0), INVALID),
+    (dict(split=24), INVALID), (dict(split=-16), INVALID), (dict(wl=-2), INVALID),
+    (dict(Hkv=3), INVALID), (dict(d=32), UNSUPPORTED), (dict(scale=0.0), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws=P + 16), WORKSPACE), (dict(wsb=1024), WORKSPACE),
+    (dict(B=70000), INVALID),
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+def _golden_cu():
+    path = os.path.join(ROOT, "tests", "golden", "cu_seqlens_examples.txt")
+    rows = []
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        lens, cu = line.split("|")
+        rows.append(([int(x) for x in lens.split()], [int(x) for x in cu.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("lens,cu", _golden_cu())
+def test_cu_seqlens_worked_examples(lens, cu):
+    if lens:
+        assert fa.cu_seqlens_from_lengths(lens).tolist() == cu
+    assert fa.cu_seqlens_from_lengths(fa.lengths_from_cu_seqlens(cu)).tolist() == cu
+    assert fa.lengths_from_cu_seqlens(cu).sum() == cu[-1]
+
+
+def test_cu_seqlens_rejects_bad_input():
+    with pytest.raises(ValueError):
+        fa.cu_seqlens_from_lengths([3, -1])
+    with pytest.raises(ValueError):
+        fa.lengths_from_cu_seqlens([1, 4])
+    with pytest.raises(ValueError):
+        fa.lengths_from_cu_seqlens([0, 5, 3])
+
+
+def test_binding_requires_device_tensors(lib):
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q)
+
+
+def test_no_oracle_import_in_product():
+    """The product package never imports or references the oracle."""
+    pkg = os.path.join(ROOT, "exact_attention_17_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt, f

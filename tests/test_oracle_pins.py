@@ -430,3 +430,13 @@ def test_planted_mistakes_are_caught(monkeypatch):
         monkeypatch.setattr(oracle_attention, "key_visibility", orig_vis)
         monkeypatch.setattr(oracle_attention, "attend_rows", orig_attend)
         monkeypatch.setattr(oracle_attention, "_kv_head", orig_head)
+
+
+def test_uint16_inputs_are_bf16_bit_patterns():
+    x = np.array([1.0, -2.5, 3.140625, 0.0, 65280.0], dtype=np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)            # exact bf16 values
+    q = bits.reshape(1, 1, 1, 5)
+    k = np.ones((1, 1, 1, 5))
+    v = bits.reshape(1, 1, 1, 5)
+    O, _ = oracle.attention_ref(q, k, v, 1.0)
+    assert np.array_equal(O[0, 0, 0], x.astype(np.float64))

@@ -1,0 +1,213 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU fp64 oracle.
+
+Small cases are compared element by element over every output; they span
+several 128-row / 64-key tiles with ragged tails and cover each mask mode,
+MHA/GQA/MQA, both head dims, Lq != Lk, fully masked rows, zero-length varlen
+sequences and paged layouts with several page sizes and split sizes.  The five
+named workloads run at full size in the launch configuration bench.py times;
+prefill outputs are checked on sampled rows the oracle computes one by one,
+the decode workload on every output.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import bits, check, dev, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_dense(fa, w):
+    o, lse = fa.fa_fwd(dev(w.q), dev(w.k), dev(w.v), w.scale, w.causal, w.window)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+# --------------------------------------------------------------- small dense
+@pytest.mark.parametrize("Hkv", [1, 2])
+def test_small_dense_workload(fa, Hkv):
+    w = workloads.small_dense(Hkv=Hkv)
+    o, lse = run_dense(fa, w)
+    O, LSE = oracle.attention_ref(bits(w.q), bits(w.k), bits(w.v), w.scale, w.causal, w.window)
+    check(w.name, o, lse, O, LSE)
+
+
+DENSE_CASES = [
+    # B, Lq, Lk, Hq, Hkv, d, causal, window
+    (2, 300, 300, 4, 2, 128, True, (-1, -1)),
+    (2, 300, 300, 4, 4, 64, False, (-1, -1)),
+    (1, 257, 257, 8, 1, 128, True, (37, 0)),
+    (1, 200, 200, 2, 2, 64, False, (50, 20)),
+    (1, 129, 385, 2, 1, 128, True, (-1, -1)),      # Lq < Lk: bottom-right causal
+    (1, 385, 129, 2, 2, 64, True, (-1, -1)),       # Lq > Lk: first rows see no key
+    (3, 64, 64, 2, 2, 128, False, (-1, 5)),        # right-only window
+    (1, 1, 77, 4, 2, 128, True, (-1, -1)),         # a single query row
+    (1, 1000, 1000, 2, 1, 64, True, (100, 0)),
+    (1, 33, 1, 2, 1, 64, False, (-1, -1)),         # one key
+    (2, 190, 190, 6, 3, 128, True, (0, 0)),        # window (0, 0): self only
+    (1, 160, 160, 4, 2, 64, False, (-1, -1)),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "-".join(map(str, c[:6])) + f"-c{int(c[6])}-w{c[7][0]}_{c[7][1]}")
+def test_dense_sweep(fa, case):
+    B, Lq, Lk, Hq, Hkv, d, causal, window = case
+    w = workloads.random_dense(100 + Lq + Lk + d + Hq, B, Lq, Lk, Hq, Hkv, d, causal, window)
+    o, lse = run_dense(fa, w)
+    O, LSE = oracle.attention_ref(bits(w.q), bits(w.k), bits(w.v), w.scale, causal, window)
+    check(f"dense{case}", o, lse, O, LSE)
+
+
+def test_dense_rescale_stress(fa):
+    """Scores that rise along the keys force the running max up on every tile."""
+    B, L, H, d = 1, 512, 2, 128
+    w = workloads.random_dense(77, B, L, L, H, H, d, True)
+    k = w.k.float()
+    qdir = w.q.float()[:, -1:, :, :] / w.q.float()[:, -1:, :, :].norm(dim=-1, keepdim=True)
+    ramp = torch.linspace(0, 24, L).view(1, L, 1, 1)
+    w.k = (k + ramp * qdir).to(torch.bfloat16)
+    o, lse = run_dense(fa, w)
+    O, LSE = oracle.attention_ref(bits(w.q), bits(w.k), bits(w.v), w.scale, True)
+    check("rescale_stress", o, lse, O, LSE)
+
+
+def test_dense_large_scale_values(fa):
+    """A large softmax scale makes P nearly one-hot; checks the max/exponent path."""
+    w = workloads.random_dense(78, 1, 256, 256, 2, 1, 64, True, scale=2.0)
+    o, lse = run_dense(fa, w)
+    O, LSE = oracle.attention_ref(bits(w.q), bits(w.k), bits(w.v), 2.0, True)
+    check("large_scale", o, lse, O, LSE)
+
+
+# -------------------------------------------------------------------- varlen
+VARLEN_CASES = [
+    ([1, 0, 7, 128, 129, 300], 4, 2, 128, True, (-1, -1)),
+    ([1, 0, 7, 128, 129, 300], 4, 4, 64, True, (50, 0)),
+    ([250, 3, 64], 2, 1, 64, False, (-1, -1)),
+    ([513, 17], 8, 8, 128, False, (30, 30)),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: f"n{len(c[0])}-h{c[1]}-kv{c[2]}-d{c[3]}-c{int(c[4])}-w{c[5][0]}")
+def test_varlen_sweep(fa, case):
+    lens, Hq, Hkv, d, causal, window = case
+    w = workloads.random_varlen(200 + sum(lens) + d, lens, Hq, Hkv, d, causal, window)
+    cu = dev(torch.from_numpy(w.cu_seqlens))
+    o, lse = fa.fa_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), cu, cu, w.max_seqlen, w.max_seqlen,
+                              w.scale, causal, window)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_varlen_ref(bits(w.q), bits(w.k), bits(w.v), w.cu_seqlens,
+                                         w.cu_seqlens, w.scale, causal, window)
+    check(f"varlen{case}", o.cpu(), lse.cpu(), O, LSE)
+
+
+# -------------------------------------------------------------------- decode
+def run_decode(fa, w, split=None, window_left=None):
+    out = fa.fa_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache),
+                             dev(torch.from_numpy(w.block_table)), dev(torch.from_numpy(w.seqlens)),
+                             w.scale, w.window_left if window_left is None else window_left,
+                             w.split_tokens if split is None else split)
+    torch.cuda.synchronize()
+    return out[0].cpu(), out[1].cpu()
+
+
+def decode_ref(w, window_left=None):
+    return oracle.decode_paged_ref(bits(w.q), bits(w.k_cache), bits(w.v_cache), w.block_table,
+                                   w.seqlens, w.page_size, w.scale,
+                                   w.window_left if window_left is None else window_left)
+
+
+DECODE_CASES = [
+    # lens, Hq, Hkv, d, page_size, split, window_left
+    ([1, 15, 16, 17, 511, 512, 513, 1000], 8, 2, 128, 16, 512, -1),
+    ([1, 15, 16, 17, 511, 512, 513, 1000], 8, 2, 128, 16, 16, -1),
+    ([300, 64, 900], 4, 4, 64, 16, 0, -1),
+    ([300, 7, 900], 8, 1, 128, 8, 128, -1),        # MQA, page_size 8 (< 16)
+    ([333, 1, 64], 4, 2, 128, 1, 64, -1),          # page_size 1
+    ([700, 129], 32, 2, 128, 32, 256, -1),         # 16 heads per KV head: two 8-row groups
+    ([1000, 50], 6, 2, 64, 16, 512, 100),          # 3 heads per KV head, window
+    ([0, 40], 4, 2, 128, 16, 512, -1),             # an empty cache
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"n{len(c[0])}-h{c[1]}-kv{c[2]}-d{c[3]}-p{c[4]}-s{c[5]}-w{c[6]}")
+def test_decode_sweep(fa, case):
+    lens, Hq, Hkv, d, ps, split, wl = case
+    npages = sum(-(-l // ps) for l in lens) + 3
+    w = workloads.random_paged(300 + sum(lens) + ps, lens, Hq, Hkv, d, ps, npages, split,
+                               max_blocks=max(1, -(-max(lens) // ps)) + 2, window_left=wl)
+    o, lse = run_decode(fa, w)
+    O, LSE = decode_ref(w)
+    check(f"decode{case}", o, lse, O, LSE)
+
+
+# ---------------------------------------------------------- full workloads
+def sampled_rows(L, rng, extra=12):
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, L // 2, L - 129, L - 128, L - 2, L - 1]
+    rnd = rng.integers(0, L, extra).tolist()
+    return np.unique(np.clip(fixed + rnd, 0, L - 1))
+
+
+def check_dense_sampled(name, w, o, lse, pairs, rng):
+    qb, kb, vb = bits(w.q), bits(w.k), bits(w.v)
+    o_np, lse_np = f64(o), f64(lse)
+    assert np.isfinite(o_np).all() and np.isfinite(lse_np).all()
+    vmax = np.abs(f64(w.v)).max()
+    assert np.abs(o_np).max() <= vmax * (1 + 1e-2) + 4e-3        # convex combination of V rows
+    L = w.q.shape[1]
+    worst = (0.0, 0.0)
+    for b, h in pairs:
+        rows = sampled_rows(L, rng)
+        O, LSE = oracle.attention_rows_ref(qb, kb, vb, b, h, rows, w.scale, w.causal, w.window)
+        r = check(f"{name} b{b} h{h}", o_np[b, rows, h], lse_np[b, h, rows], O, LSE)
+        worst = (max(worst[0], r[0]), max(worst[1], r[1]))
+    return worst
+
+
+def test_full_causal_mha(fa):
+    w = workloads.causal_mha()
+    o, lse = run_dense(fa, w)
+    rng = np.random.default_rng(2)
+    pairs = [(0, 0), (1, 7), (2, 19), (3, 31), (3, 0), (0, 16)]
+    check_dense_sampled(w.name, w, o, lse, pairs, rng)
+
+
+def test_full_causal_gqa_long(fa):
+    w = workloads.causal_gqa_long()
+    o, lse = run_dense(fa, w)
+    rng = np.random.default_rng(3)
+    pairs = [(0, 0), (0, 3), (0, 4), (0, 17), (0, 30), (0, 31)]
+    check_dense_sampled(w.name, w, o, lse, pairs, rng)
+
+
+def test_full_paged_decode(fa):
+    w = workloads.paged_decode()
+    o, lse = run_decode(fa, w)
+    O, LSE = decode_ref(w)
+    check(w.name, o, lse, O, LSE)
+
+
+def test_full_varlen_window(fa):
+    w = workloads.varlen_window()
+    cu = dev(torch.from_numpy(w.cu_seqlens))
+    o, lse = fa.fa_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), cu, cu, w.max_seqlen, w.max_seqlen,
+                              w.scale, w.causal, w.window)
+    torch.cuda.synchronize()
+    o, lse = f64(o.cpu()), f64(lse.cpu())
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    qb, kb, vb = bits(w.q), bits(w.k), bits(w.v)
+    rng = np.random.default_rng(5)
+    H = w.q.shape[1]
+    for b, L in enumerate(w.lens):
+        s = int(w.cu_seqlens[b])
+        rows = sampled_rows(int(L), rng, extra=4)
+        rows = np.unique(np.concatenate([rows, np.clip([4095, 4096, 4097, 4098], 0, L - 1)]))
+        for h in (b % H, (b * 7 + 3) % H):
+            O, LSE = oracle.attention_rows_ref(qb[None, s:s + L], kb[None, s:s + L], vb[None, s:s + L],
+                                               0, h, rows, w.scale, w.causal, w.window)
+            check(f"{w.name} seq{b} h{h}", o[s + rows, h], lse[h, s + rows], O, LSE)
