@@ -40,7 +40,8 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E (published)
 METRIC = "prefill attn TFLOP/s (% MFMA peak); paged-decode KV GB/s (% HBM peak)"
 PREFILL_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "prefill_fwd.hip")
 DECODE_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "decode_paged.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 512 << 20             # plain device copy used to calibrate the byte counters
 
 
 def visible_pairs(Lq, Lk, causal, wl, wr):
@@ -95,14 +96,31 @@ def time_calls(fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
-def load_traffic(kernel_key, src):
+def load_traffic(summary_name, src):
+    """HBM bytes per launch from a committed counter summary (profiles/<name>.md),
+    or None if missing or if the kernel source changed since it was taken."""
+    vals = {}
     try:
-        t = json.load(open(TRAFFIC_FILE))[kernel_key]
-    except (OSError, KeyError, ValueError):
+        for line in open(os.path.join(PROFILES, summary_name + ".md")):
+            if ":" in line and line.strip().startswith(("bytes_per_launch", "source_sha256_16")):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    except OSError:
         return None
-    if t.get("source_sha256_16") != file_hash(src):
+    if vals.get("source_sha256_16") != file_hash(src) or "bytes_per_launch" not in vals:
         return None
-    return t.get("bytes_per_launch")
+    return float(vals["bytes_per_launch"])
+
+
+def copy_calibration(reps=5):
+    """A plain device-to-device copy of COPY_BYTES, so a counter run sees the
+    FETCH_SIZE / WRITE_SIZE that a kernel of known traffic produces."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(w, flops_total):
@@ -136,6 +154,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time only the main workload")
+    ap.add_argument("--only-decode", action="store_true", help="time only the paged decode workload")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain copy of known size (for byte-counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -148,14 +169,32 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     props = torch.cuda.get_device_properties(0)
+    if args.copy_calibration:
+        copy_calibration()
 
-    # ---------------------------------------------------------- main workload
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic", "device": props.name}
     w2 = workloads.causal_mha()
+    flops2 = dense_flops(w2)
+    if not args.only_decode:
+        result.update(bench_main(fa, w2, flops2, args))
+    wl = {}
+    if not args.only_main:
+        wl, roof_dec = bench_others(fa, args)
+        result["roofline_decode"] = roof_dec
+    result["workloads"] = wl
+    if not args.no_cpu_baseline and not args.only_decode:
+        result["cpu_baseline"] = cpu_baseline(w2, flops2)
+    print(json.dumps(result), flush=True)
+
+
+def bench_main(fa, w2, flops2, args):
+    """The contract step: K timed fa_fwd calls on the causal MHA workload."""
     q, k, v = w2.q.cuda(), w2.k.cuda(), w2.v.cuda()
     o = torch.empty_like(q)
     lse = torch.empty((4, 32, 2048), dtype=torch.float32, device="cuda")
     step = lambda: fa.fa_fwd(q, k, v, w2.scale, True, (-1, -1), out=o, lse=lse)
-    flops2 = dense_flops(w2)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -167,25 +206,22 @@ def main():
     ev_ms = time_calls(step, args.steps, 2)
     value = flops2 / (wall_ms * 1e-3) / 1e12
     achieved = flops2 / (ev_ms * 1e-3) / 1e12
-    traffic = load_traffic("prefill_fwd_causal_mha", PREFILL_SRC)
-    result = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
+    traffic = load_traffic("prefill_fwd_causal_mha_traffic", PREFILL_SRC)
+    return {
+        "value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(wall_ms, 4),
         "config": {"workload": w2.name, "B": 4, "Hq": 32, "Hkv": 32, "L": 2048, "d": 128,
                    "causal": True, "flops_per_step": flops2},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "prefill_fwd_kernel<128,false>",
                      "avg_launch_ms": round(ev_ms, 4)},
-        "device": props.name,
     }
-    del q, k, v, o, lse
 
-    # ------------------------------------------------------- other workloads
+
+def bench_others(fa, args):
+    """Time the remaining workloads; returns (per-workload dict, decode roofline)."""
     wl = {}
-    if not args.only_main:
+    if not args.only_decode:
         w1 = workloads.small_dense(Hkv=1)
         a = [t.cuda() for t in (w1.q, w1.k, w1.v)]
         ms = time_calls(lambda: fa.fa_fwd(*a, w1.scale, False), args.steps, args.warmup)
@@ -211,31 +247,27 @@ def main():
                                "frac_mfma": round(f5 / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": f5}
         del a, w5
 
-        w4 = workloads.paged_decode()
-        qd, kc, vc = w4.q.cuda(), w4.k_cache.cuda(), w4.v_cache.cuda()
-        bt = torch.from_numpy(w4.block_table).cuda()
-        sl = torch.from_numpy(w4.seqlens).cuda()
-        ws = torch.empty(fa.fa_decode_paged_workspace_size(64, 32, 128, bt.shape[1], 16, 512),
-                         dtype=torch.uint8, device="cuda")
-        od = torch.empty_like(qd)
-        ld = torch.empty((64, 32), dtype=torch.float32, device="cuda")
-        nb = decode_bytes(w4)
-        ms = time_calls(lambda: fa.fa_decode_paged(qd, kc, vc, bt, sl, w4.scale, -1, 512, out=od,
-                                                   lse=ld, workspace=ws), args.steps, args.warmup)
-        gbs = nb / ms / 1e6
-        wl["paged_decode"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
-                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb,
-                              "kernels": "decode_split + decode_merge"}
-        result["roofline_decode"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                     "traffic": load_traffic("decode_paged", DECODE_SRC)}
-        del qd, kc, vc, w4
-        torch.cuda.empty_cache()
-    result["workloads"] = wl
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w2, flops2)
-    print(json.dumps(result), flush=True)
+    w4 = workloads.paged_decode()
+    qd, kc, vc = w4.q.cuda(), w4.k_cache.cuda(), w4.v_cache.cuda()
+    bt = torch.from_numpy(w4.block_table).cuda()
+    sl = torch.from_numpy(w4.seqlens).cuda()
+    ws = torch.empty(fa.fa_decode_paged_workspace_size(64, 32, 128, bt.shape[1], 16, 512),
+                     dtype=torch.uint8, device="cuda")
+    od = torch.empty_like(qd)
+    ld = torch.empty((64, 32), dtype=torch.float32, device="cuda")
+    nb = decode_bytes(w4)
+    ms = time_calls(lambda: fa.fa_decode_paged(qd, kc, vc, bt, sl, w4.scale, -1, 512, out=od,
+                                               lse=ld, workspace=ws), args.steps, args.warmup)
+    gbs = nb / ms / 1e6
+    wl["paged_decode"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
+                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb,
+                          "kernels": "decode_split + decode_merge"}
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic("decode_paged_traffic", DECODE_SRC)}
+    del qd, kc, vc, w4
+    torch.cuda.empty_cache()
+    return wl, roof
 
 
 if __name__ == "__main__":

@@ -82,6 +82,17 @@ FA_DEV float row16_sum(float x) {
   return x;
 }
 
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives 16-bit element i%4 of the 8-byte rows addressed by lanes
+// i/4, 4+i/4, 8+i/4 and 12+i/4.  So if lane j addresses row r0 + j/4, column
+// c0 + 4*(j%4) of a row-major matrix, lane i gets column c0 + i of rows
+// r0..r0+3: a 4x16 block comes back transposed.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+FA_DEV u32x2 tr_read_b64(const uint16_t* lds) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)lds));
+}
+
 FA_DEV bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Raw buffer resource over [base, base + bytes).  A load whose byte offset is

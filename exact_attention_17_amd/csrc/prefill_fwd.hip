@@ -14,19 +14,23 @@
 //
 // Mapping onto CDNA4 (our design, not the pages'):
 //   * A workgroup is 4 wave64s and owns 128 query rows of one (batch, head);
-//     each wave owns 32 rows.  The loop walks 64-key tiles of K and V.
+//     each wave owns 32 rows.  Two workgroups share a CU (two waves per SIMD),
+//     so one wave's MFMAs overlap the other's softmax.  The loop walks
+//     64-key tiles of K and V.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: K rows are the A operand (from LDS), the
 //     wave's Q rows are the B operand and stay in registers for the whole
-//     loop.  In the accumulator each lane then holds ONE query (column) and
-//     16 keys per 32x32 tile, so the row max is an in-lane max plus one
-//     exchange between the two wave halves, and the row sum needs no
-//     cross-lane work until the epilogue.
+//     loop.  In the accumulator each lane holds ONE query (column) and 16 keys per
+//     32x32 tile, so the row max is an in-lane max plus one exchange between
+//     the two wave halves, and the row sum needs no cross-lane work until the
+//     epilogue.
 //   * The same accumulator registers, rounded to bf16, are exactly the B
 //     operand of the PV product computed as O^T = V^T P^T: no LDS round trip
-//     for P.  The A operand V^T needs 4 consecutive keys per lane at a fixed
-//     d, so V is transposed while it is staged into LDS (register shuffles
-//     with v_perm_b32 and 8-byte LDS writes).
+//     for P.  V stays row-major in LDS; its A operand (4 consecutive keys per
+//     lane at a fixed d) comes from ds_read_b64_tr_b16 transpose reads.
+//   * Software pipeline across tiles: while the softmax of tile j runs on the
+//     VALU, the MFMAs of S^T for tile j+1 are issued in the same basic block,
+//     then P_j V_j follows; K runs one tile ahead of V in the LDS buffers.
 //   * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score.
 //     The reference max used in the exponent is only raised when a row's max
 //     exceeds it by more than 2^8 (wave-uniform branch), so the output
@@ -46,6 +50,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 namespace fa {
 
 namespace {
@@ -53,17 +59,16 @@ namespace {
 constexpr float kRescaleTau = 8.0f;   // log2 units: rescale only if max grows > 2^8
 constexpr float kLn2 = 0.6931471805599453f;
 
-// LDS tile layouts (element units are bf16).  Rows are padded so that the
-// MFMA operand reads of 32 different rows hit different banks while every
-// address stays affine (one base register plus immediate offsets).
-//   K tile   [64 keys][D + 8]: a 16-byte read per lane, 8 lanes per bank cycle.
-//   V^T tile [D rows][64 + 4]: 4 keys (8 bytes) per lane, 16 lanes per cycle.
+// LDS tile layouts (element units are bf16), both row-major with padded rows:
+//   K [64 keys][D + 8]: 16-byte MFMA operand reads of 8 consecutive rows hit
+//     8 distinct 4-bank groups (row stride = 4 banks mod 32).
+//   V [64 keys][D + 16]: a transpose read has 4 rows x 32 bytes per 16-lane
+//     group; a row stride of 8 banks mod 32 spreads them over all 32 banks.
 template <int D> struct Lds {
   static constexpr int kStride = D + 8;
-  static constexpr int vStride = kBlockN + 4;
+  static constexpr int vStride = D + 16;
   static constexpr int kTile = kBlockN * kStride;
-  static constexpr int vTile = D * vStride;
-  static constexpr int stage = kTile + vTile;
+  static constexpr int vTile = kBlockN * vStride;
 };
 
 struct WorkItem {
@@ -136,17 +141,17 @@ void prefill_fwd_kernel(PrefillParams p) {
   constexpr int KSTEPS = D / 16;                 // QK^T MFMA steps over d
   constexpr int DBLK = D / 32;                   // 32-row blocks of O^T
   constexpr int KCH = D / 8;                     // 16-byte chunks per row
-  constexpr int K_LOADS = kBlockN * KCH / kPrefillThreads;
-  constexpr int K_ROWS_PER_PASS = kPrefillThreads / KCH;
-  constexpr int V_ITEMS = (kBlockN / 4) * KCH;   // 4 keys x 8 d per item
-  constexpr int STAGE = Lds<D>::stage;           // K tile + V^T tile (bf16 elements)
+  constexpr int LOADS = kBlockN * KCH / kPrefillThreads;
+  constexpr int ROWS_PER_PASS = kPrefillThreads / KCH;
   constexpr int KS = Lds<D>::kStride, VS = Lds<D>::vStride;
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * Lds<D>::kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2 * Lds<D>::vTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hi = lane >> 5;
+  const int i16 = lane & 15, g16 = lane >> 4;
 
   const WorkItem w = VARLEN ? map_work_varlen(p, blockIdx.x) : map_work_dense(p, blockIdx.x);
   if (!w.valid) return;
@@ -190,11 +195,9 @@ void prefill_fwd_kernel(PrefillParams p) {
   const int ntiles = kt_end - kt_begin;
 
   const int qw0 = q0 + 32 * wave;
-  const bool wave_rows = qw0 < Lq;
-  const int rw0 = qw0, rw1 = min(qw0 + 31, Lq - 1);
-  const int wlo_first = key_lo(rw0), wlo_last = key_lo(rw1);
-  const int whi_first = key_hi(rw0), whi_last = key_hi(rw1);
-  const int row = qw0 + n;                       // this lane's query row
+  const int rw0 = min(qw0, Lq - 1), rw1 = min(qw0 + 31, Lq - 1);
+  const int wlo_last = key_lo(rw1), whi_first = key_hi(rw0);
+  const int row = qw0 + n;
   const int my_lo = key_lo(row), my_hi = key_hi(row);
 
   // ---- Q fragments (B operand), resident for the whole loop --------------
@@ -209,154 +212,152 @@ void prefill_fwd_kernel(PrefillParams p) {
     for (int t = 0; t < KSTEPS; ++t) qf[t] = buf_load16(qr, off + 32u * t);
   }
 
-  // ---- staging of one K/V tile: global -> registers -> LDS ----------------
-  u32x4 kreg[K_LOADS];
-  u32x4 vreg[4];
-  const int kc = tid % KCH, kr0 = tid / KCH;
-  // V items (4 keys x 8 d): 16 lanes of one LDS write phase take 8 key groups x
-  // 2 d-chunks, so (d + key group) mod 16 -- the bank pair -- is distinct.
-  const int vkg = (tid & 7) | (((tid >> 4) & 1) << 3);
-  const int vdc = ((tid >> 3) & 1) | ((tid >> 5) << 1);
-  const bool v_active = tid < V_ITEMS;
-
+  // ---- staging of K/V tiles: global -> registers -> LDS (row-major) -------
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, k_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, k_bytes);
-  auto load_tile = [&](int kb) {
+  const int sc = tid % KCH, sr = tid / KCH;
+  u32x4 kreg[LOADS], vreg[LOADS];
+  // Byte offsets grow with the key, so rows at or past Lk fall outside the
+  // buffer range (k_bytes) and load as zeros without a compare.  Offsets stay
+  // below 2^32: per-batch tensors are < 2^31 bytes and a tile adds < 2^24.
+  auto load_rows = [&](const __amdgpu_buffer_rsrc_t& rs, u32x4 (&reg)[LOADS], int kb) {
+    const uint32_t base = (uint32_t)(kb + sr) * k_row_bytes + sc * 16u;
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int key = kb + kr0 + i * K_ROWS_PER_PASS;
-      const uint32_t off = key < Lk ? (uint32_t)key * k_row_bytes + kc * 16u : kOob;
-      kreg[i] = buf_load16(krs, off);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kb + 4 * vkg + i;
-      const uint32_t off = (v_active && key < Lk) ? (uint32_t)key * k_row_bytes + vdc * 16u : kOob;
-      vreg[i] = buf_load16(vrs, off);
-    }
+    for (int i = 0; i < LOADS; ++i) reg[i] = buf_load16(rs, base + (uint32_t)(i * ROWS_PER_PASS) * k_row_bytes);
   };
-  auto store_tile = [&](int stage) {
-    uint16_t* ks = smem + stage * STAGE;
-    uint16_t* vs = ks + Lds<D>::kTile;
+  auto store_rows = [&](uint16_t* base, int stride, const u32x4 (&reg)[LOADS]) {
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int r = kr0 + i * K_ROWS_PER_PASS;
-      *reinterpret_cast<u32x4*>(ks + r * KS + kc * 8) = kreg[i];
-    }
-    if (v_active) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t w0 = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
-        const uint32_t w1 = __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel);
-        *reinterpret_cast<u32x2*>(vs + (vdc * 8 + e) * VS + vkg * 4) = u32x2{w0, w1};
-      }
-    }
+    for (int i = 0; i < LOADS; ++i)
+      *reinterpret_cast<u32x4*>(base + (sr + i * ROWS_PER_PASS) * stride + sc * 8) = reg[i];
   };
 
-  // ---- running state ------------------------------------------------------
+  // ---- the per-tile phases ---------------------------------------------------
+  // S^T = K Q^T for the two 32-key halves of a tile (K fragments of a half are
+  // read from LDS together, ahead of their MFMAs).
+  auto qk = [&](int buf, f32x16 (&S)[2]) {
+    const uint16_t* ks = k_lds + buf * Lds<D>::kTile + n * KS + hi * 8;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      u32x4 a[KSTEPS];
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) a[t] = *reinterpret_cast<const u32x4*>(ks + 32 * kh * KS + 16 * t);
+      S[kh] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) S[kh] = mfma32x32x16(a[t], qf[t], S[kh]);
+    }
+  };
+  // mask only on tiles that cut through some row's visible band
+  auto mask_tile = [&](f32x16 (&S)[2], int kb) {
+    if (kb >= wlo_last && kb + kBlockN <= whi_first) return;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + 32 * kh + 8 * (r >> 2) + 4 * hi + (r & 3);
+        S[kh][r] = (key >= my_lo && key < my_hi) ? S[kh][r] : -INFINITY;
+      }
+  };
+  // P = 2^(S*c - m) as packed bf16 MFMA fragments; l sums the unrounded fp32
+  // P (two chains), which keeps LSE to fp32 accuracy.
+  float m_ref = -INFINITY;
+  float l_a = 0.f, l_b = 0.f;
+  const float c = p.scale_log2;
   f32x16 oacc[DBLK];
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
-  float m_ref = -INFINITY;   // reference max, log2 units
-  float l_sum = 0.f;         // partial row sum over this lane's half of the keys
-  const float c = p.scale_log2;
-
-  if (ntiles > 0) {
-    load_tile(kt_begin * kBlockN);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int stage = it & 1;
-    const int kb = (kt_begin + it) * kBlockN;
-    if (it + 1 < ntiles) load_tile(kb + kBlockN);
-
-    const bool active = wave_rows && kb < whi_last && kb + kBlockN > wlo_first;
-    if (active) {
-      const uint16_t* ks = smem + stage * STAGE;
-      const uint16_t* vs = ks + Lds<D>::kTile;
-      // S^T = K Q^T for two 32-key halves of the tile
-      f32x16 sacc[2];
+  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
+  // Row max of the tile (log2 units); raise the reference max only when it
+  // grows by more than 2^8 and rescale O and l then (rare: wave-uniform branch).
+  auto update_max = [&](const f32x16 (&S)[2]) {
+    float mx = S[0][0];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        sacc[kb2] = f32x16{};
-        const int key = 32 * kb2 + n;
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[0][r]);
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(ks + key * KS + (2 * t + hi) * 8);
-          sacc[kb2] = mfma32x32x16(a, qf[t], sacc[kb2]);
-        }
-      }
-      // mask only on tiles that cut through some row's visible band
-      const bool full = kb >= wlo_last && kb + kBlockN <= whi_first;
-      if (!full) {
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[1][r]);
+    mx = fmaxf(mx, xor32(mx)) * c;
+    const bool up = mx > m_ref + kRescaleTau;
+    // a row that has seen no key yet has O = 0 and l = 0: nothing to rescale
+    if (wave_any(up && m_ref != -INFINITY)) {
+      const float alpha = up ? exp2_fast(m_ref - mx) : 1.f;
+      l_a *= alpha;
+      l_b *= alpha;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+    }
+    if (up) m_ref = mx;
+  };
+  auto softmax = [&](const f32x16 (&S)[2], u32x4 (&P)[4]) {
+    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb + 32 * kb2 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            sacc[kb2][r] = (key >= my_lo && key < my_hi) ? sacc[kb2][r] : -INFINITY;
-          }
-        }
-      }
-      // row max over the tile: in-lane, then across the two wave halves
-      float mx = sacc[0][0];
+    for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-      mx = fmaxf(mx, xor32(mx));
-      const float tmax = mx * c;
-      const bool up = tmax > m_ref + kRescaleTau;
-      if (wave_any(up)) {
-        const float m_new = up ? tmax : m_ref;
-        const float alpha = up ? exp2_fast(m_ref - m_new) : 1.f;
-        l_sum *= alpha;
-#pragma unroll
-        for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
-        m_ref = m_new;
-      }
-      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
-      // P = 2^(S*c - m): fp32 exponentials, bf16 fragments for the PV MFMA
-      u32x4 pf[4];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        float pv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pv[r] = exp2_fast(fmaf(sacc[kb2][r], c, -mb));
-          l_sum += pv[r];
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          pf[2 * kb2 + hh] = u32x4{pack_bf16x2(pv[8 * hh + 0], pv[8 * hh + 1]),
-                                   pack_bf16x2(pv[8 * hh + 2], pv[8 * hh + 3]),
-                                   pack_bf16x2(pv[8 * hh + 4], pv[8 * hh + 5]),
-                                   pack_bf16x2(pv[8 * hh + 6], pv[8 * hh + 7])};
-        }
-      }
-      // O^T += V^T P^T, 16 keys per MFMA
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int d = 32 * db + n;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vs + d * VS + (4 * cc + hi) * 4);
-          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vs + d * VS + (4 * cc + 2 + hi) * 4);
-          const u32x4 a = u32x4{lo[0], lo[1], hi2[0], hi2[1]};
-          oacc[db] = mfma32x32x16(a, pf[cc], oacc[db]);
-        }
+      for (int r2 = 0; r2 < 8; ++r2) {
+        const float p0 = exp2_fast(fmaf(S[kh][2 * r2], c, -mb));
+        const float p1 = exp2_fast(fmaf(S[kh][2 * r2 + 1], c, -mb));
+        l_a += p0;
+        l_b += p1;
+        P[2 * kh + (r2 >> 2)][r2 & 3] = pack_bf16x2(p0, p1);
       }
     }
+  };
+  // O^T += V^T P^T: V^T fragments from transpose reads of the row-major tile;
+  // lane i of a 16-lane group addresses key row i/4 and d column 4*(i%4).
+  const int tr_off = (4 * hi + (i16 >> 2)) * VS + 16 * (g16 & 1) + 4 * (i16 & 3);
+  auto pv = [&](int buf, const u32x4 (&P)[4]) {
+    const uint16_t* vs = v_lds + buf * Lds<D>::vTile + tr_off;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      u32x4 a[DBLK];
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const u32x2 lo = tr_read_b64(vs + (16 * cc) * VS + 32 * db);
+        const u32x2 hi2 = tr_read_b64(vs + (16 * cc + 8) * VS + 32 * db);
+        a[db] = u32x4{lo[0], lo[1], hi2[0], hi2[1]};
+      }
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) oacc[db] = mfma32x32x16(a[db], P[cc], oacc[db]);
+    }
+  };
 
-    if (it + 1 < ntiles) store_tile(stage ^ 1);
+  // ---- prologue: K(0), K(1), V(0) into LDS; S^T(0) -------------------------
+  const int kb0 = kt_begin * kBlockN;
+  load_rows(krs, kreg, kb0);
+  load_rows(vrs, vreg, kb0);
+  store_rows(k_lds, KS, kreg);
+  store_rows(v_lds, VS, vreg);
+  load_rows(krs, kreg, kb0 + kBlockN);
+  store_rows(k_lds + Lds<D>::kTile, KS, kreg);
+  __syncthreads();
+  f32x16 s0[2], s1[2];
+  u32x4 pf[4];
+  if (ntiles > 0) qk(0, s0);
+
+  // ---- main loop: two tiles per trip with ping-pong score buffers ---------
+  // Tile j: S^T(j) is ready.  K(j+2) and V(j+1) are fetched while tile j is
+  // computed, and S^T(j+1) is issued in the same basic block as the softmax
+  // of tile j, so MFMA and VALU work overlap.  K runs one tile ahead of V.
+  // (the parity of j, and so every LDS buffer offset, is a compile-time constant)
+  auto step = [&](auto parity, int j, f32x16 (&Scur)[2], f32x16 (&Snxt)[2]) {
+    constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
+    const int kb = kb0 + j * kBlockN;
+    mask_tile(Scur, kb);
+    update_max(Scur);
+    load_rows(krs, kreg, kb + 2 * kBlockN);
+    load_rows(vrs, vreg, kb + kBlockN);
+    qk(nxt, Snxt);
+    softmax(Scur, pf);
+    pv(cur, pf);
+    store_rows(k_lds + cur * Lds<D>::kTile, KS, kreg);
+    store_rows(v_lds + nxt * Lds<D>::vTile, VS, vreg);
     __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    step(std::integral_constant<int, 0>{}, j, s0, s1);
+    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1, s1, s0);
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2 ------------
-  const float lt = l_sum + xor32(l_sum);
+  const float lpart = l_a + l_b;
+  const float lt = lpart + xor32(lpart);
   if (row < Lq) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     uint16_t* orow = og + (int64_t)row * p.q_tok_stride;
