@@ -23,7 +23,7 @@
 //     per-wave LDS buffer; P*V runs on the fp32 VALU with V read in fully
 //     coalesced 256-byte rows.  The four waves merge in LDS and write one
 //     partial (O_s normalised, LSE_s) per query head.
-//   * decode_merge: one workgroup per (request, query head) combines the
+//   * decode_merge: one wave per (request, query head) combines the
 //     partials by their LSE and writes bf16 O and fp32 LSE.
 //   * Keys at or past a request's length (and before its window) never reach
 //     the result: they read a safe in-bounds cache row (never an unused
@@ -60,8 +60,11 @@ void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float o_lds[4][GR][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = blockIdx.x, b = blockIdx.z;
-  const int kvh = blockIdx.y / p.sub_groups, sub = blockIdx.y % p.sub_groups;
+  // grid = (KV head x head subgroup, split, request): the workgroups of all KV
+  // heads of one split are dispatched together, so the heads interleaved in
+  // each cache page are read at the same time (DRAM row locality).
+  const int s = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.x / p.sub_groups, sub = blockIdx.x % p.sub_groups;
   const int h0 = kvh * p.group + sub * GR;
   const int nrow = min(GR, p.group - sub * GR);
 
@@ -288,10 +291,15 @@ void decode_split_kernel(DecodeParams p) {
   }
 }
 
+// One wave per (request, query head).  Lanes first take one split each to find
+// the largest partial LSE and the total weight; then every lane owns d/64
+// output columns and sums the weighted partials with all loads of a group of
+// splits issued before their use.
 template <int D>
-__global__ __launch_bounds__(128)
+__global__ __launch_bounds__(64)
 void decode_merge_kernel(DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  constexpr int PER = D / 64;
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int len = p.seqlens[b];
   const int lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
   const int s_beg = lo / p.split_tokens;
@@ -301,24 +309,44 @@ void decode_merge_kernel(DecodeParams p) {
   const float* po = p.part_o + row * p.max_splits * D;
 
   float M = -INFINITY;
-  for (int s = s_beg; s < s_end; ++s) M = fmaxf(M, plse[s]);
-  float wsum = 0.f, acc = 0.f;
-  for (int s = s_beg; s < s_end; ++s) {
-    const float wgt = exp2_fast(plse[s] - M);
-    wsum += wgt;
-    if (tid < D) acc += wgt * po[(int64_t)s * D + tid];
+  for (int s = s_beg + lane; s < s_end; s += 64) M = fmaxf(M, plse[s]);
+  for (int off = 32; off > 0; off >>= 1)
+    M = fmaxf(M, __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(M))));
+  float wsum = 0.f;
+  for (int s = s_beg + lane; s < s_end; s += 64) wsum += exp2_fast(plse[s] - M);
+  for (int off = 32; off > 0; off >>= 1)
+    wsum += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ off) << 2, __float_as_int(wsum)));
+
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int s0 = s_beg; s0 < s_end; s0 += 8) {
+    float wv[8], ov[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, s_end - 1);
+      wv[u] = plse[s];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) ov[u][e] = po[(int64_t)s * D + lane + 64 * e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wgt = (s0 + u < s_end) ? exp2_fast(wv[u] - M) : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wgt, ov[u][e], acc[e]);
+    }
   }
   const bool empty = s_end <= s_beg;
-  if (tid < D) {
-    const float out = empty ? 0.f : acc / wsum;
-    p.o[row * D + tid] = (uint16_t)(pack_bf16x2(out, 0.f) & 0xffffu);
-  }
-  if (p.lse && tid == 0) p.lse[row] = empty ? -INFINITY : (M + log2_fast(wsum)) * kLn2;
+  const float inv = empty ? 0.f : 1.f / wsum;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    p.o[row * D + lane + 64 * e] = (uint16_t)(pack_bf16x2(acc[e] * inv, 0.f) & 0xffffu);
+  if (p.lse && lane == 0) p.lse[row] = empty ? -INFINITY : (M + log2_fast(wsum)) * kLn2;
 }
 
 template <int D, bool PAGE16>
 static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
-  const dim3 grid(p.max_splits, p.Hkv * p.sub_groups, p.B), block(kDecodeThreads);
+  const dim3 grid(p.Hkv * p.sub_groups, p.max_splits, p.B), block(kDecodeThreads);
   switch (rows) {
     case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, PAGE16>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, PAGE16>), grid, block, 0, stream, p); break;
@@ -333,7 +361,7 @@ static hipError_t launch_decode_d(const DecodeParams& p, int rows, hipStream_t s
   else launch_split<D, false>(p, rows, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid2(p.Hq, p.B), block2(128);
+  const dim3 grid2(p.Hq, p.B), block2(64);
   hipLaunchKernelGGL((decode_merge_kernel<D>), grid2, block2, 0, stream, p);
   return hipGetLastError();
 }

@@ -170,7 +170,9 @@ fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cach
     return FA_ERR_INVALID_ARG;
   if (num_pages < 1) return FA_ERR_INVALID_ARG;
   if (!decode_sizes_ok(B, Hq, d, max_blocks_per_seq, page_size, split_tokens)) return FA_ERR_INVALID_ARG;
-  if (B > 65535 || (int64_t)Hkv * cdiv(Hq / Hkv, pow2_rows(Hq / Hkv)) > 65535) return FA_ERR_INVALID_ARG;
+  // launch grid: (Hkv * head subgroups, splits, B); the merge grid is (Hq, B)
+  if (B > 65535 || cdiv((int64_t)max_blocks_per_seq * page_size, effective_split(split_tokens)) > 65535)
+    return FA_ERR_INVALID_ARG;
   if ((int64_t)num_pages * page_size * Hkv * d >= ((int64_t)1 << 40)) return FA_ERR_INVALID_ARG;
   const size_t need = fa_decode_paged_workspace_size(B, Hq, d, max_blocks_per_seq, page_size, split_tokens);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return FA_ERR_WORKSPACE;

@@ -330,6 +330,8 @@ void prefill_fwd_kernel(PrefillParams p) {
   f32x16 s0[2], s1[2];
   u32x4 pf[4];
   if (ntiles > 0) qk(0, s0);
+  // step 0 overwrites K buffer 0 with K(2): every wave must be done reading K(0)
+  __syncthreads();
 
   // ---- main loop: two tiles per trip with ping-pong score buffers ---------
   // Tile j: S^T(j) is ready.  K(j+2) and V(j+1) are fetched while tile j is

@@ -113,3 +113,16 @@ def test_decode_equals_last_prefill_row(fa):
     assert np.abs(a - b).max() <= 2 * (4e-3 + 1e-2 * np.abs(b).max())
     assert abs(float(lse_dec[0, 0]) - float(lse_pre.cpu()[0, 0, -1])) <= 2e-4
     check("decode_vs_oracle_row", o_dec[0, 0, :1].float(), lse_dec[0, :1], O, LSE)
+
+
+def test_repeated_runs_are_bitwise_identical(fa):
+    """Many short workgroups, run repeatedly: an LDS reuse race between waves
+    would show up as run-to-run differences."""
+    for case in [(1, 160, 160, 4, 2, 64, False, (-1, -1)), (2, 300, 300, 4, 2, 128, True, (-1, -1))]:
+        B, Lq, Lk, Hq, Hkv, d, causal, window = case
+        w = workloads.random_dense(31, B, Lq, Lk, Hq, Hkv, d, causal, window)
+        q, k, v = dev(w.q), dev(w.k), dev(w.v)
+        ref = fa.fa_fwd(q, k, v, w.scale, causal, window)
+        for _ in range(30):
+            o, lse = fa.fa_fwd(q, k, v, w.scale, causal, window)
+            assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), case
