@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
@@ -87,6 +89,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.causal = causal; p.win_left = window_left; p.win_right = window_right;
   p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
   p.xcd_groups = xcd_groups(B * Hkv);
+  // KV groups per XCD chunk: about one XCD's worth of resident workgroups
+  p.chunk_groups = (int)std::max<int64_t>(1, fa::kPrefillSlotsPerXcd / ((int64_t)p.group * p.num_q_tiles));
   if ((int64_t)p.num_q_tiles * B * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
   hipError_t e = fa::launch_prefill(p, d, false, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -17,6 +17,8 @@ constexpr int kBlockN = 64;
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeChunk = 64;     // keys per wave iteration
 constexpr int kDefaultSplit = 512;
+// Prefill workgroups resident per XCD (32 CUs x 2), used to size work chunks.
+constexpr int kPrefillSlotsPerXcd = 64;
 
 struct PrefillParams {
   const uint16_t* q;       // bf16 bits
@@ -37,6 +39,7 @@ struct PrefillParams {
   int causal, win_left, win_right;
   int num_q_tiles;         // dense: ceil(Lq / kBlockM); varlen: total tile slots
   int xcd_groups;          // >0: XCD-aware work mapping with this many KV groups
+  int chunk_groups;        // KV groups an XCD works on together (dense mapping)
 };
 
 struct DecodeParams {

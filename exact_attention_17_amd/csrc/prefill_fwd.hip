@@ -41,9 +41,10 @@
 //     it.  Rows past a sequence end come back as zeros from the buffer range
 //     check.  LDS rows are padded so MFMA operand reads and the staging
 //     writes avoid bank conflicts with affine addresses.
-//   * Workgroup order: heavy causal tiles first; when the KV-group count is a
-//     multiple of 8, all query heads of a KV group land on one XCD (blocks are
-//     dealt to the 8 XCDs round-robin), so its K/V stays in one L2.
+//   * Workgroup order: when the KV-group count is a multiple of 8, all query
+//     heads of a KV group land on one XCD (blocks are dealt to the 8 XCDs
+//     round-robin), a few KV groups at a time so their K/V stays in that L2;
+//     within such a chunk heavy causal tiles go first.
 #include "fa_internal.h"
 #include "gfx950.h"
 
@@ -78,13 +79,24 @@ struct WorkItem {
   bool valid;
 };
 
+// Dense work order.  Blocks are dealt to the 8 XCDs round-robin (block id % 8),
+// so when the KV-group count (B * Hkv) is a multiple of 8, XCD x gets KV groups
+// x, x+8, ...  Within an XCD the groups are taken in chunks of `chunk_groups`
+// (sized so a chunk's workgroups about fill the XCD), and inside a chunk the
+// query tiles go heaviest (latest causal rows) first.  A chunk's K/V then
+// stays in the XCD's L2 while all its query tiles stream through it.
 __device__ __forceinline__ WorkItem map_work_dense(const PrefillParams& p, int id) {
   WorkItem w;
   if (p.xcd_groups > 0) {
     const int x = id & 7, s = id >> 3;
-    const int per = (p.xcd_groups >> 3) * p.group;      // query heads per XCD
-    const int qrev = s / per, r = s - qrev * per;
-    const int gl = r / p.group, gq = r - gl * p.group;
+    const int A = p.xcd_groups >> 3;                   // KV groups per XCD
+    const int per_group = p.group * p.num_q_tiles;     // workgroups per KV group
+    const int chunk = s / (p.chunk_groups * per_group);
+    const int c0 = chunk * p.chunk_groups;
+    const int cn = min(p.chunk_groups, A - c0);        // groups in this chunk
+    const int sl = s - c0 * per_group;
+    const int qrev = sl / (cn * p.group), r = sl - qrev * (cn * p.group);
+    const int gl = c0 + r / p.group, gq = r % p.group;
     const int kvg = x + 8 * gl;
     w.b = kvg / p.Hkv;
     w.h = (kvg - w.b * p.Hkv) * p.group + gq;
@@ -320,12 +332,15 @@ void prefill_fwd_kernel(PrefillParams p) {
 
   // ---- prologue: K(0), K(1), V(0) into LDS; S^T(0) -------------------------
   const int kb0 = kt_begin * kBlockN;
-  load_rows(krs, kreg, kb0);
-  load_rows(vrs, vreg, kb0);
-  store_rows(k_lds, KS, kreg);
-  store_rows(v_lds, VS, vreg);
-  load_rows(krs, kreg, kb0 + kBlockN);
-  store_rows(k_lds + Lds<D>::kTile, KS, kreg);
+  {
+    u32x4 k1reg[LOADS];   // all three prologue tiles in flight at once
+    load_rows(krs, kreg, kb0);
+    load_rows(vrs, vreg, kb0);
+    load_rows(krs, k1reg, kb0 + kBlockN);
+    store_rows(k_lds, KS, kreg);
+    store_rows(v_lds, VS, vreg);
+    store_rows(k_lds + Lds<D>::kTile, KS, k1reg);
+  }
   __syncthreads();
   f32x16 s0[2], s1[2];
   u32x4 pf[4];
