@@ -18,8 +18,9 @@
 //     split_tokens keys).  Each wave takes 64-key chunks of the split.
 //     Scores for the group's query heads come from v_mfma_f32_16x16x32_bf16
 //     with the (zero-padded) query heads as the 16-row A operand and K rows
-//     as the B operand, loaded straight from the cache in MFMA layout (each
-//     lane reads 16 contiguous bytes of one key row).  P goes through a small
+//     as the B operand.  K and V rows are both read so that each 16-lane
+//     group covers one full 256-byte row; K then goes through a per-wave LDS
+//     tile into the MFMA operand order.  P goes through a small
 //     per-wave LDS buffer; P*V runs on the fp32 VALU with V read in fully
 //     coalesced 256-byte rows.  The four waves merge in LDS and write one
 //     partial (O_s normalised, LSE_s) per query head.
@@ -54,10 +55,15 @@ void decode_split_kernel(DecodeParams p) {
   constexpr int VLOADS = kDecodeChunk / VKEYS;
   constexpr int PST = GR < 4 ? 4 : GR;    // P row stride in the LDS buffer (floats)
 
+  constexpr int KST = D + 8;               // padded K row in the per-wave staging tile
+  static_assert(GR * D * 4 <= kDecodeChunk * KST * 2, "wave partial must fit its K tile");
   __shared__ __attribute__((aligned(16))) float p_lds[4][kDecodeChunk][PST];
   __shared__ float a_lds[4][16];
   __shared__ float m_lds[4][GR], l_lds[4][GR];
-  __shared__ __attribute__((aligned(16))) float o_lds[4][GR][D];
+  // Per-wave K tile [64 keys][D + 8]; after a wave's last chunk its region
+  // holds that wave's partial O (GR x D floats) for the workgroup merge.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[4][kDecodeChunk * KST];
+  auto o_part = [&](int w_) { return reinterpret_cast<float*>(&k_lds[w_][0]); };   // [GR][D]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // grid = (KV head x head subgroup, split, request): the workgroups of all KV
@@ -128,12 +134,14 @@ void decode_split_kernel(DecodeParams p) {
       const int pid = ok ? bt[key / p.page_size] : 0;
       return (int64_t)pid * p.page_size + (ok ? key % p.page_size : 0);
     };
+    // K rows are read like V rows (a 16-lane group covers 256 contiguous bytes),
+    // then re-laid out through the wave's LDS tile into the MFMA operand order.
     u32x4 kr[4][KT];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const uint16_t* src = kcache + row_of(kc + 16 * blk + sn, blk) * tok_stride + 8 * sg;
-#pragma unroll
-      for (int t = 0; t < KT; ++t) kr[blk][t] = *reinterpret_cast<const u32x4*>(src + 32 * t);
+    for (int i = 0; i < VLOADS; ++i) {
+      const int key = kc + VKEYS * i + vj;
+      const uint16_t* src = kcache + row_of(key, (VKEYS * i) / 16) * tok_stride + 8 * vc;
+      kr[i / KT][i % KT] = *reinterpret_cast<const u32x4*>(src);
     }
     u32x4 vr[VLOADS];
 #pragma unroll
@@ -148,6 +156,19 @@ void decode_split_kernel(DecodeParams p) {
         const int key = kc + VKEYS * i + vj;
         if (!(key >= k_beg && key < k_end)) vr[i] = u32x4{0, 0, 0, 0};
       }
+    }
+    {
+      uint16_t* kt = k_lds[wave];
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i)
+        *reinterpret_cast<u32x4*>(kt + (VKEYS * i + vj) * KST + 8 * vc) = kr[i / KT][i % KT];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+          kr[blk][t] = *reinterpret_cast<const u32x4*>(kt + (16 * blk + sn) * KST + 32 * t + 8 * sg);
+      __builtin_amdgcn_wave_barrier();
     }
     // ---- scores S = Q K^T (rows = query heads, columns = 16 keys per block)
     f32x4 sacc[4];
@@ -263,9 +284,9 @@ void decode_split_kernel(DecodeParams p) {
   if (vj == 0) {
 #pragma unroll
     for (int r = 0; r < GR; ++r) {
-      *reinterpret_cast<f32x4*>(&o_lds[wave][r][8 * vc]) =
+      *reinterpret_cast<f32x4*>(o_part(wave) + r * D + 8 * vc) =
           f32x4{oacc[r][0], oacc[r][1], oacc[r][2], oacc[r][3]};
-      *reinterpret_cast<f32x4*>(&o_lds[wave][r][8 * vc + 4]) =
+      *reinterpret_cast<f32x4*>(o_part(wave) + r * D + 8 * vc + 4) =
           f32x4{oacc[r][4], oacc[r][5], oacc[r][6], oacc[r][7]};
     }
   }
@@ -283,7 +304,7 @@ void decode_split_kernel(DecodeParams p) {
     for (int w = 0; w < 4; ++w) {
       const float f = m_lds[w][r] == -INFINITY ? 0.f : exp2_fast(m_lds[w][r] - M);
       lsum += f * l_lds[w][r];
-      osum += f * o_lds[w][r][d];
+      osum += f * o_part(w)[r * D + d];
     }
     const int64_t slot = ((int64_t)b * p.Hq + h0 + r) * p.max_splits + s;
     p.part_o[slot * D + d] = osum / lsum;
