@@ -93,6 +93,21 @@ FA_DEV u32x2 tr_read_b64(const uint16_t* lds) {
       u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)lds));
 }
 
+// Byte address of a __shared__ object in the workgroup's LDS window.
+FA_DEV uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// 16-byte buffer load that writes LDS instead of VGPRs: lane l stores its 16
+// bytes at LDS byte lds_base + 16 l (lds_base must be wave-uniform; it goes
+// in M0).  Out-of-range lanes store zeros.  The compiler does not track these
+// loads, so lds_load_wait() must run before the data is read.
+FA_DEV void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(r), "{m0}"(lds_base) : "memory");
+}
+FA_DEV void lds_load_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 FA_DEV bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Raw buffer resource over [base, base + bytes).  A load whose byte offset is

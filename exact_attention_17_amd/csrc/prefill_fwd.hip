@@ -36,11 +36,12 @@
 //     exceeds it by more than 2^8 (wave-uniform branch), so the output
 //     rescale is skipped on almost every tile; P stays <= 256 and the final
 //     division by l makes the result exact either way.
-//   * K/V tiles are double-buffered in LDS: the buffer loads of tile j+1 are
-//     issued before tile j is computed and written to the other buffer after
-//     it.  Rows past a sequence end come back as zeros from the buffer range
-//     check.  LDS rows are padded so MFMA operand reads and the staging
-//     writes avoid bank conflicts with affine addresses.
+//   * K/V tiles are double-buffered in LDS and filled by buffer loads that
+//     write LDS directly (no VGPR staging, no ds_write): the loads of K(j+2)
+//     and V(j+1) are issued at the start of tile j and awaited at its end.
+//     Rows past a sequence end come back as zeros from the buffer range
+//     check.  16-byte chunks are XOR-swizzled within each row so the MFMA
+//     operand reads and the transpose reads avoid LDS bank conflicts.
 //   * Workgroup order: when the KV-group count is a multiple of 8, all query
 //     heads of a KV group land on one XCD (blocks are dealt to the 8 XCDs
 //     round-robin), a few KV groups at a time so their K/V stays in that L2;
@@ -60,16 +61,20 @@ namespace {
 constexpr float kRescaleTau = 8.0f;   // log2 units: rescale only if max grows > 2^8
 constexpr float kLn2 = 0.6931471805599453f;
 
-// LDS tile layouts (element units are bf16), both row-major with padded rows:
-//   K [64 keys][D + 8]: 16-byte MFMA operand reads of 8 consecutive rows hit
-//     8 distinct 4-bank groups (row stride = 4 banks mod 32).
-//   V [64 keys][D + 16]: a transpose read has 4 rows x 32 bytes per 16-lane
-//     group; a row stride of 8 banks mod 32 spreads them over all 32 banks.
+// LDS tile layouts: K and V tiles are [64 keys][D] bf16, row-major and
+// unpadded, because the direct-to-LDS loads write 1 KB contiguous blocks.  The
+// 16-byte chunk c of row r is stored at chunk c ^ swz(r):
+//   K (D=128): swz = r & 15 -- an MFMA operand read (16 bytes per lane, lane n
+//     on row n) puts 16 consecutive rows on 16 distinct 16-byte bank groups;
+//   K (D=64):  swz = (r & 7) ^ ((r >> 3) & 1) -- rows are 128 bytes, so row
+//     parity also picks the bank half;
+//   V (D=128): swz = {0, 6, 12, 10}[r & 3] and V (D=64): swz = 2 (r & 3) -- a
+//     transpose read touches 4 rows x 4 chunks per 32 lanes; these put them on
+//     16 distinct bank groups (and any 16 lanes on 8).
 template <int D> struct Lds {
-  static constexpr int kStride = D + 8;
-  static constexpr int vStride = D + 16;
-  static constexpr int kTile = kBlockN * kStride;
-  static constexpr int vTile = kBlockN * vStride;
+  static constexpr int kTile = kBlockN * D;   // bf16 elements per K or V tile
+  FA_DEV static int kswz(int r) { return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)); }
+  FA_DEV static int vswz(int r) { return D == 128 ? ((r & 1) * 6) ^ (((r >> 1) & 1) * 12) : 2 * (r & 3); }
 };
 
 struct WorkItem {
@@ -153,12 +158,12 @@ void prefill_fwd_kernel(PrefillParams p) {
   constexpr int KSTEPS = D / 16;                 // QK^T MFMA steps over d
   constexpr int DBLK = D / 32;                   // 32-row blocks of O^T
   constexpr int KCH = D / 8;                     // 16-byte chunks per row
-  constexpr int LOADS = kBlockN * KCH / kPrefillThreads;
-  constexpr int ROWS_PER_PASS = kPrefillThreads / KCH;
-  constexpr int KS = Lds<D>::kStride, VS = Lds<D>::vStride;
+  constexpr int RPI = 64 / KCH;                  // rows per 1 KB load instruction
+  constexpr int LOADS = kBlockN / RPI / 4;       // load instructions per wave per tile
+  constexpr int TILE_BYTES = Lds<D>::kTile * 2;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * Lds<D>::kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2 * Lds<D>::vTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * Lds<D>::kTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2 * Lds<D>::kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -224,35 +229,45 @@ void prefill_fwd_kernel(PrefillParams p) {
     for (int t = 0; t < KSTEPS; ++t) qf[t] = buf_load16(qr, off + 32u * t);
   }
 
-  // ---- staging of K/V tiles: global -> registers -> LDS (row-major) -------
+  // ---- staging of K/V tiles: global -> LDS directly ------------------------
+  // Load instruction i of wave w fills tile bytes [(4i + w) KB, +1 KB): rows
+  // (4i + w) * RPI + lane / KCH, stored chunk lane % KCH, which holds logical
+  // chunk (lane % KCH) ^ swz(row).  Byte offsets grow with the key, so rows at
+  // or past Lk fall outside the buffer range (k_bytes) and load as zeros.
+  // Offsets stay below 2^32: per-batch tensors are < 2^31 bytes and a tile
+  // adds < 2^24.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, k_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, k_bytes);
-  const int sc = tid % KCH, sr = tid / KCH;
-  u32x4 kreg[LOADS], vreg[LOADS];
-  // Byte offsets grow with the key, so rows at or past Lk fall outside the
-  // buffer range (k_bytes) and load as zeros without a compare.  Offsets stay
-  // below 2^32: per-batch tensors are < 2^31 bytes and a tile adds < 2^24.
-  auto load_rows = [&](const __amdgpu_buffer_rsrc_t& rs, u32x4 (&reg)[LOADS], int kb) {
-    const uint32_t base = (uint32_t)(kb + sr) * k_row_bytes + sc * 16u;
+  uint32_t k_src[LOADS], v_src[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) reg[i] = buf_load16(rs, base + (uint32_t)(i * ROWS_PER_PASS) * k_row_bytes);
-  };
-  auto store_rows = [&](uint16_t* base, int stride, const u32x4 (&reg)[LOADS]) {
+  for (int i = 0; i < LOADS; ++i) {
+    const int r = (4 * i + wave) * RPI + lane / KCH, slot = lane % KCH;
+    k_src[i] = (uint32_t)r * k_row_bytes + (uint32_t)((slot ^ Lds<D>::kswz(r)) * 16);
+    v_src[i] = (uint32_t)r * k_row_bytes + (uint32_t)((slot ^ Lds<D>::vswz(r)) * 16);
+  }
+  const uint32_t k_lds_addr = lds_address(k_lds), v_lds_addr = lds_address(v_lds);
+  const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
+  auto fetch = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t (&src)[LOADS], uint32_t dst, int kb) {
+    const uint32_t off = (uint32_t)kb * k_row_bytes;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      *reinterpret_cast<u32x4*>(base + (sr + i * ROWS_PER_PASS) * stride + sc * 8) = reg[i];
+    for (int i = 0; i < LOADS; ++i) lds_load16(rs, src[i] + off, dst + wave_lds + 4096u * i);
   };
 
   // ---- the per-tile phases ---------------------------------------------------
   // S^T = K Q^T for the two 32-key halves of a tile (K fragments of a half are
   // read from LDS together, ahead of their MFMAs).
+  // Lane (key n, half hi) reads logical chunk 2t + hi of rows n and 32 + n
+  // (same swizzle: the two rows differ by 32).
+  uint32_t k_rd[KSTEPS];
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) k_rd[t] = (uint32_t)(n * D + (((2 * t + hi) ^ Lds<D>::kswz(n)) * 8));
   auto qk = [&](int buf, f32x16 (&S)[2]) {
-    const uint16_t* ks = k_lds + buf * Lds<D>::kTile + n * KS + hi * 8;
+    const uint16_t* ks = k_lds + buf * Lds<D>::kTile;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       u32x4 a[KSTEPS];
 #pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) a[t] = *reinterpret_cast<const u32x4*>(ks + 32 * kh * KS + 16 * t);
+      for (int t = 0; t < KSTEPS; ++t) a[t] = *reinterpret_cast<const u32x4*>(ks + k_rd[t] + 32 * kh * D);
       S[kh] = f32x16{};
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) S[kh] = mfma32x32x16(a[t], qf[t], S[kh]);
@@ -311,18 +326,25 @@ void prefill_fwd_kernel(PrefillParams p) {
       }
     }
   };
-  // O^T += V^T P^T: V^T fragments from transpose reads of the row-major tile;
-  // lane i of a 16-lane group addresses key row i/4 and d column 4*(i%4).
-  const int tr_off = (4 * hi + (i16 >> 2)) * VS + 16 * (g16 & 1) + 4 * (i16 & 3);
+  // O^T += V^T P^T: V^T fragments from transpose reads of the row-major tile.
+  // Lane i of a 16-lane group g addresses key row 16cc + 8j + 4hi + i/4 and
+  // the 8-byte unit 8db + 4(g&1) + (i&3) of it, i.e. half i&1 of logical
+  // chunk 4db + 2(g&1) + (i&3)/2; the row's swizzle depends on i/4 only.
+  uint32_t v_rd[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    const int chunk = 4 * db + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+    v_rd[db] = (uint32_t)((4 * hi + (i16 >> 2)) * D + ((chunk ^ Lds<D>::vswz(i16 >> 2)) * 8) + 4 * (i16 & 1));
+  }
   auto pv = [&](int buf, const u32x4 (&P)[4]) {
-    const uint16_t* vs = v_lds + buf * Lds<D>::vTile + tr_off;
+    const uint16_t* vs = v_lds + buf * Lds<D>::kTile;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       u32x4 a[DBLK];
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        const u32x2 lo = tr_read_b64(vs + (16 * cc) * VS + 32 * db);
-        const u32x2 hi2 = tr_read_b64(vs + (16 * cc + 8) * VS + 32 * db);
+        const u32x2 lo = tr_read_b64(vs + v_rd[db] + (16 * cc) * D);
+        const u32x2 hi2 = tr_read_b64(vs + v_rd[db] + (16 * cc + 8) * D);
         a[db] = u32x4{lo[0], lo[1], hi2[0], hi2[1]};
       }
 #pragma unroll
@@ -332,39 +354,39 @@ void prefill_fwd_kernel(PrefillParams p) {
 
   // ---- prologue: K(0), K(1), V(0) into LDS; S^T(0) -------------------------
   const int kb0 = kt_begin * kBlockN;
-  {
-    u32x4 k1reg[LOADS];   // all three prologue tiles in flight at once
-    load_rows(krs, kreg, kb0);
-    load_rows(vrs, vreg, kb0);
-    load_rows(krs, k1reg, kb0 + kBlockN);
-    store_rows(k_lds, KS, kreg);
-    store_rows(v_lds, VS, vreg);
-    store_rows(k_lds + Lds<D>::kTile, KS, k1reg);
+  if (ntiles > 0) {
+    fetch(krs, k_src, k_lds_addr, kb0);
+    fetch(vrs, v_src, v_lds_addr, kb0);
+    if (ntiles > 1) fetch(krs, k_src, k_lds_addr + TILE_BYTES, kb0 + kBlockN);
   }
+  lds_load_wait();
   __syncthreads();
   f32x16 s0[2], s1[2];
   u32x4 pf[4];
-  if (ntiles > 0) qk(0, s0);
-  // step 0 overwrites K buffer 0 with K(2): every wave must be done reading K(0)
+  // Unconditional, so the Q loads are awaited here on every path: the compiler
+  // does not see the direct-to-LDS loads, and a Q wait left pending into the
+  // loop would be counted against them there.
+  qk(0, s0);
+  // step 0 loads K(2) into K buffer 0: every wave must be done reading K(0)
   __syncthreads();
 
   // ---- main loop: two tiles per trip with ping-pong score buffers ---------
-  // Tile j: S^T(j) is ready.  K(j+2) and V(j+1) are fetched while tile j is
-  // computed, and S^T(j+1) is issued in the same basic block as the softmax
-  // of tile j, so MFMA and VALU work overlap.  K runs one tile ahead of V.
+  // Tile j: S^T(j) is ready.  K(j+2) and V(j+1) are loaded into the buffers
+  // of K(j) and V(j-1), whose last reads finished before the barrier that
+  // ended tile j-1, while tile j is computed; S^T(j+1) is issued in the same
+  // basic block as the softmax of tile j, so MFMA and VALU work overlap.
   // (the parity of j, and so every LDS buffer offset, is a compile-time constant)
   auto step = [&](auto parity, int j, f32x16 (&Scur)[2], f32x16 (&Snxt)[2]) {
     constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
     const int kb = kb0 + j * kBlockN;
     mask_tile(Scur, kb);
     update_max(Scur);
-    load_rows(krs, kreg, kb + 2 * kBlockN);
-    load_rows(vrs, vreg, kb + kBlockN);
+    if (j + 2 < ntiles) fetch(krs, k_src, k_lds_addr + cur * TILE_BYTES, kb + 2 * kBlockN);
+    if (j + 1 < ntiles) fetch(vrs, v_src, v_lds_addr + nxt * TILE_BYTES, kb + kBlockN);
     qk(nxt, Snxt);
     softmax(Scur, pf);
     pv(cur, pf);
-    store_rows(k_lds + cur * Lds<D>::kTile, KS, kreg);
-    store_rows(v_lds + nxt * Lds<D>::vTile, VS, vreg);
+    lds_load_wait();
     __syncthreads();
   };
   for (int j = 0; j < ntiles; j += 2) {
