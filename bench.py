@@ -6,6 +6,11 @@ A step is one fa_fwd call on the causal MHA prefill workload (B=4, H=32,
 L=2048, d=128, bf16, seeded synthetic inputs resident in HBM).  The timed
 region is exactly K steps bracketed by torch.cuda.synchronize(); `value` is
 algorithmic TFLOP/s (4*d FLOPs per visible (query, key) pair per head).
+
+Before the W warmup steps each workload runs untimed for --prewarm-ms of wall
+time: the GPU raises its engine clock only after some milliseconds of
+sustained load, and without this the first tens of milliseconds (the whole
+timed region at small K) run at a lower clock.
 The other workloads (long-context GQA prefill, paged decode, varlen window
 prefill, the small dense case) are timed in the same run and reported under
 "workloads".  One JSON line is printed.
@@ -81,9 +86,20 @@ def file_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def time_calls(fn, steps, warmup):
+def prewarm(fn, ms):
+    """Call fn back to back for about `ms` of wall time (untimed), syncing every
+    few calls so the launch queue stays short."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_calls(fn, steps, warmup, prewarm_ms=0.0):
     """Average ms per call from HIP events recorded on the launch stream
     (torch's current stream, which the binding launches on)."""
+    prewarm(fn, prewarm_ms)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -150,8 +166,10 @@ def cpu_baseline(w, flops_total):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-ms", type=float, default=300.0,
+                    help="untimed back-to-back calls before the warmup steps of each workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time only the main workload")
     ap.add_argument("--only-decode", action="store_true", help="time only the paged decode workload")
@@ -174,7 +192,7 @@ def main():
 
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-              "data": "synthetic", "device": props.name}
+              "data": "synthetic", "device": props.name, "prewarm_ms": args.prewarm_ms}
     w2 = workloads.causal_mha()
     flops2 = dense_flops(w2)
     if not args.only_decode:
@@ -195,6 +213,7 @@ def bench_main(fa, w2, flops2, args):
     o = torch.empty_like(q)
     lse = torch.empty((4, 32, 2048), dtype=torch.float32, device="cuda")
     step = lambda: fa.fa_fwd(q, k, v, w2.scale, True, (-1, -1), out=o, lse=lse)
+    prewarm(step, args.prewarm_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -224,14 +243,14 @@ def bench_others(fa, args):
     if not args.only_decode:
         w1 = workloads.small_dense(Hkv=1)
         a = [t.cuda() for t in (w1.q, w1.k, w1.v)]
-        ms = time_calls(lambda: fa.fa_fwd(*a, w1.scale, False), args.steps, args.warmup)
+        ms = time_calls(lambda: fa.fa_fwd(*a, w1.scale, False), args.steps, args.warmup, args.prewarm_ms)
         wl["small_dense"] = {"ms": round(ms, 4), "TFLOP/s": round(dense_flops(w1) / ms / 1e9, 3)}
         del a
 
         w3 = workloads.causal_gqa_long()
         a = [t.cuda() for t in (w3.q, w3.k, w3.v)]
         f3 = dense_flops(w3)
-        ms = time_calls(lambda: fa.fa_fwd(*a, w3.scale, True), max(5, args.steps // 5), 3)
+        ms = time_calls(lambda: fa.fa_fwd(*a, w3.scale, True), max(5, args.steps // 10), 3, args.prewarm_ms)
         wl["causal_gqa_long"] = {"ms": round(ms, 4), "TFLOP/s": round(f3 / ms / 1e9, 2),
                                  "frac_mfma": round(f3 / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
                                  "flops": f3}
@@ -242,7 +261,8 @@ def bench_others(fa, args):
         cu = torch.from_numpy(w5.cu_seqlens).cuda()
         f5 = varlen_flops(w5)
         ms = time_calls(lambda: fa.fa_fwd_varlen(*a, cu, cu, w5.max_seqlen, w5.max_seqlen, w5.scale,
-                                                 True, w5.window), args.steps, args.warmup)
+                                                 True, w5.window), args.steps, args.warmup,
+                        args.prewarm_ms)
         wl["varlen_window"] = {"ms": round(ms, 4), "TFLOP/s": round(f5 / ms / 1e9, 2),
                                "frac_mfma": round(f5 / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": f5}
         del a, w5
@@ -257,7 +277,8 @@ def bench_others(fa, args):
     ld = torch.empty((64, 32), dtype=torch.float32, device="cuda")
     nb = decode_bytes(w4)
     ms = time_calls(lambda: fa.fa_decode_paged(qd, kc, vc, bt, sl, w4.scale, -1, 512, out=od,
-                                               lse=ld, workspace=ws), args.steps, args.warmup)
+                                               lse=ld, workspace=ws), args.steps, args.warmup,
+                    args.prewarm_ms)
     gbs = nb / ms / 1e6
     wl["paged_decode"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
                           "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb,
