@@ -98,13 +98,15 @@ FA_DEV uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
-// 16-byte buffer load that writes LDS instead of VGPRs: lane l stores its 16
-// bytes at LDS byte lds_base + 16 l (lds_base must be wave-uniform; it goes
-// in M0).  Out-of-range lanes store zeros.  The compiler does not track these
-// loads, so lds_load_wait() must run before the data is read.
-FA_DEV void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voffset), "s"(r), "{m0}"(lds_base) : "memory");
+// 16-byte buffer load that writes LDS instead of VGPRs: lane l reads bytes
+// [voffset + soffset, +16) of the buffer and stores them at LDS byte
+// lds_base + 16 l (soffset and lds_base must be wave-uniform; lds_base goes
+// in M0).  The range check applies to voffset + soffset: out-of-range lanes
+// store zeros.  The compiler does not track these loads, so lds_load_wait()
+// must run before the data is read.
+FA_DEV void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(lds_base) : "memory");
 }
 FA_DEV void lds_load_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -28,9 +28,11 @@
 //     operand of the PV product computed as O^T = V^T P^T: no LDS round trip
 //     for P.  V stays row-major in LDS; its A operand (4 consecutive keys per
 //     lane at a fixed d) comes from ds_read_b64_tr_b16 transpose reads.
-//   * Software pipeline across tiles: while the softmax of tile j runs on the
-//     VALU, the MFMAs of S^T for tile j+1 are issued in the same basic block,
-//     then P_j V_j follows; K runs one tile ahead of V in the LDS buffers.
+//   * Software pipeline across tiles: step j issues the MFMAs of S^T for tile
+//     j+1 and of P_{j-1} V_{j-1} while the softmax of tile j runs on the VALU,
+//     interleaved instruction by instruction (a wave64 MFMA 32x32x16 keeps
+//     the matrix core busy for 32 cycles, enough to issue about 5 independent
+//     VALU ops beside it).  K runs one tile ahead and V one tile behind.
 //   * Softmax runs in base 2 with scale*log2(e) folded into one FMA per score.
 //     The reference max used in the exponent is only raised when a row's max
 //     exceeds it by more than 2^8 (wave-uniform branch), so the output
@@ -161,6 +163,7 @@ void prefill_fwd_kernel(PrefillParams p) {
   constexpr int RPI = 64 / KCH;                  // rows per 1 KB load instruction
   constexpr int LOADS = kBlockN / RPI / 4;       // load instructions per wave per tile
   constexpr int TILE_BYTES = Lds<D>::kTile * 2;
+  static_assert(TILE_BYTES % (16 * kPrefillThreads) == 0, "V tile zero fill");
 
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * Lds<D>::kTile];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2 * Lds<D>::kTile];
@@ -232,45 +235,45 @@ void prefill_fwd_kernel(PrefillParams p) {
   // ---- staging of K/V tiles: global -> LDS directly ------------------------
   // Load instruction i of wave w fills tile bytes [(4i + w) KB, +1 KB): rows
   // (4i + w) * RPI + lane / KCH, stored chunk lane % KCH, which holds logical
-  // chunk (lane % KCH) ^ swz(row).  Byte offsets grow with the key, so rows at
-  // or past Lk fall outside the buffer range (k_bytes) and load as zeros.
-  // Offsets stay below 2^32: per-batch tensors are < 2^31 bytes and a tile
-  // adds < 2^24.
+  // chunk (lane % KCH) ^ swz(row).  swz(row) does not depend on i, so each lane
+  // keeps one byte offset per tensor and the uniform part (tile and i) goes in
+  // the scalar offset.  The range check covers both, so rows at or past Lk
+  // fall outside the buffer (k_bytes) and load as zeros.  Offsets stay below
+  // 2^32: per-batch tensors are < 2^31 bytes and a tile adds < 2^24.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, k_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vg, k_bytes);
-  uint32_t k_src[LOADS], v_src[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int r = (4 * i + wave) * RPI + lane / KCH, slot = lane % KCH;
-    k_src[i] = (uint32_t)r * k_row_bytes + (uint32_t)((slot ^ Lds<D>::kswz(r)) * 16);
-    v_src[i] = (uint32_t)r * k_row_bytes + (uint32_t)((slot ^ Lds<D>::vswz(r)) * 16);
+  uint32_t k_src, v_src;
+  {
+    const int r = wave * RPI + lane / KCH, slot = lane % KCH;
+    k_src = (uint32_t)r * k_row_bytes + (uint32_t)((slot ^ Lds<D>::kswz(r)) * 16);
+    v_src = (uint32_t)r * k_row_bytes + (uint32_t)((slot ^ Lds<D>::vswz(r)) * 16);
   }
   const uint32_t k_lds_addr = lds_address(k_lds), v_lds_addr = lds_address(v_lds);
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
-  auto fetch = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t (&src)[LOADS], uint32_t dst, int kb) {
-    const uint32_t off = (uint32_t)kb * k_row_bytes;
+  auto fetch = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t src, uint32_t dst, int kb) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) lds_load16(rs, src[i] + off, dst + wave_lds + 4096u * i);
+    for (int i = 0; i < LOADS; ++i) {
+      const uint32_t soff = (uint32_t)(kb + 4 * i * RPI) * k_row_bytes;
+      lds_load16(rs, src, (uint32_t)__builtin_amdgcn_readfirstlane(soff), dst + wave_lds + 4096u * i);
+    }
   };
 
   // ---- the per-tile phases ---------------------------------------------------
-  // S^T = K Q^T for the two 32-key halves of a tile (K fragments of a half are
-  // read from LDS together, ahead of their MFMAs).
-  // Lane (key n, half hi) reads logical chunk 2t + hi of rows n and 32 + n
-  // (same swizzle: the two rows differ by 32).
-  uint32_t k_rd[KSTEPS];
-#pragma unroll
-  for (int t = 0; t < KSTEPS; ++t) k_rd[t] = (uint32_t)(n * D + (((2 * t + hi) ^ Lds<D>::kswz(n)) * 8));
+  // S^T = K Q^T for the two 32-key halves of a tile.  Lane (key n, half hi)
+  // reads logical chunk 2t + hi of rows n and 32 + n (same swizzle).  The
+  // stored chunk is (2t + hi) ^ swz(n), so its byte address is a per-lane base
+  // XOR 32t: one address register serves all t.
+  const uint32_t k_base = (uint32_t)(n * 2 * D) | ((16u * hi) ^ (16u * Lds<D>::kswz(n)));
+  const char* k_lds_b = reinterpret_cast<const char*>(k_lds);
+  auto k_frag = [&](int buf, int kh, int t) {
+    return *reinterpret_cast<const u32x4*>(k_lds_b + buf * TILE_BYTES + 64 * kh * D + (k_base ^ (32u * t)));
+  };
   auto qk = [&](int buf, f32x16 (&S)[2]) {
-    const uint16_t* ks = k_lds + buf * Lds<D>::kTile;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      u32x4 a[KSTEPS];
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) a[t] = *reinterpret_cast<const u32x4*>(ks + k_rd[t] + 32 * kh * D);
       S[kh] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) S[kh] = mfma32x32x16(a[t], qf[t], S[kh]);
+      for (int t = 0; t < KSTEPS; ++t) S[kh] = mfma32x32x16(k_frag(buf, kh, t), qf[t], S[kh]);
     }
   };
   // mask only on tiles that cut through some row's visible band
@@ -294,7 +297,9 @@ void prefill_fwd_kernel(PrefillParams p) {
   for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
   // Row max of the tile (log2 units); raise the reference max only when it
   // grows by more than 2^8 and rescale O and l then (rare: wave-uniform branch).
-  auto update_max = [&](const f32x16 (&S)[2]) {
+  // flush() first adds the pending P V product, which is relative to the old
+  // reference max.
+  auto update_max = [&](const f32x16 (&S)[2], auto&& flush) {
     float mx = S[0][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[0][r]);
@@ -304,6 +309,7 @@ void prefill_fwd_kernel(PrefillParams p) {
     const bool up = mx > m_ref + kRescaleTau;
     // a row that has seen no key yet has O = 0 and l = 0: nothing to rescale
     if (wave_any(up && m_ref != -INFINITY)) {
+      flush();   // pending P V products are relative to the old max
       const float alpha = up ? exp2_fast(m_ref - mx) : 1.f;
       l_a *= alpha;
       l_b *= alpha;
@@ -329,40 +335,68 @@ void prefill_fwd_kernel(PrefillParams p) {
   // O^T += V^T P^T: V^T fragments from transpose reads of the row-major tile.
   // Lane i of a 16-lane group g addresses key row 16cc + 8j + 4hi + i/4 and
   // the 8-byte unit 8db + 4(g&1) + (i&3) of it, i.e. half i&1 of logical
-  // chunk 4db + 2(g&1) + (i&3)/2; the row's swizzle depends on i/4 only.
-  uint32_t v_rd[DBLK];
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db) {
-    const int chunk = 4 * db + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-    v_rd[db] = (uint32_t)((4 * hi + (i16 >> 2)) * D + ((chunk ^ Lds<D>::vswz(i16 >> 2)) * 8) + 4 * (i16 & 1));
-  }
+  // chunk 4db + 2(g&1) + (i&3)/2; the row's swizzle depends on i/4 only, and
+  // db enters the stored chunk's byte address as XOR 64db.
+  const uint32_t v_base = (uint32_t)((4 * hi + (i16 >> 2)) * 2 * D) |
+                          (((32u * (g16 & 1)) | (16u * ((i16 & 3) >> 1))) ^ (16u * Lds<D>::vswz(i16 >> 2))) |
+                          (8u * (i16 & 1));
+  const char* v_lds_b = reinterpret_cast<const char*>(v_lds);
   auto pv = [&](int buf, const u32x4 (&P)[4]) {
-    const uint16_t* vs = v_lds + buf * Lds<D>::kTile;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      u32x4 a[DBLK];
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        const u32x2 lo = tr_read_b64(vs + v_rd[db] + (16 * cc) * D);
-        const u32x2 hi2 = tr_read_b64(vs + v_rd[db] + (16 * cc + 8) * D);
-        a[db] = u32x4{lo[0], lo[1], hi2[0], hi2[1]};
+        const char* a = v_lds_b + buf * TILE_BYTES + 16 * cc * 2 * D + (v_base ^ (64u * db));
+        const u32x2 lo = tr_read_b64(reinterpret_cast<const uint16_t*>(a));
+        const u32x2 hi2 = tr_read_b64(reinterpret_cast<const uint16_t*>(a + 16 * D));
+        oacc[db] = mfma32x32x16(u32x4{lo[0], lo[1], hi2[0], hi2[1]}, P[cc], oacc[db]);
       }
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) oacc[db] = mfma32x32x16(a[db], P[cc], oacc[db]);
     }
   };
 
-  // ---- prologue: K(0), K(1), V(0) into LDS; S^T(0) -------------------------
+  // Instruction order of the step's main block: a few K fragment reads first,
+  // then each MFMA followed by some softmax VALU ops and the next LDS reads,
+  // so reads stay a few MFMAs ahead and the VALU work hides under the MFMAs.
+  auto interleave_hint = [] {
+#ifndef IL_UP
+#define IL_UP 3
+#define IL_V1 4
+#define IL_R1 1
+#define IL_V2 3
+#define IL_R2 2
+#endif
+    __builtin_amdgcn_sched_group_barrier(0x100, IL_UP, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KSTEPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, IL_V1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, IL_R1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * DBLK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, IL_V2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, IL_R2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+  };
+
+  // ---- prologue: K(0), K(1) into LDS, V buffer 1 zeroed; S^T(0) -----------
+  // (step 0 multiplies V buffer 1 by P = 0: it must hold finite values)
   const int kb0 = kt_begin * kBlockN;
   if (ntiles > 0) {
     fetch(krs, k_src, k_lds_addr, kb0);
-    fetch(vrs, v_src, v_lds_addr, kb0);
     if (ntiles > 1) fetch(krs, k_src, k_lds_addr + TILE_BYTES, kb0 + kBlockN);
   }
+#pragma unroll
+  for (int i = 0; i < TILE_BYTES / 16 / kPrefillThreads; ++i)
+    reinterpret_cast<u32x4*>(v_lds + Lds<D>::kTile)[tid + i * kPrefillThreads] = u32x4{0u, 0u, 0u, 0u};
   lds_load_wait();
   __syncthreads();
   f32x16 s0[2], s1[2];
-  u32x4 pf[4];
+  u32x4 p0[4], p1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p1[i] = u32x4{0u, 0u, 0u, 0u};
   // Unconditional, so the Q loads are awaited here on every path: the compiler
   // does not see the direct-to-LDS loads, and a Q wait left pending into the
   // loop would be counted against them there.
@@ -370,28 +404,40 @@ void prefill_fwd_kernel(PrefillParams p) {
   // step 0 loads K(2) into K buffer 0: every wave must be done reading K(0)
   __syncthreads();
 
-  // ---- main loop: two tiles per trip with ping-pong score buffers ---------
-  // Tile j: S^T(j) is ready.  K(j+2) and V(j+1) are loaded into the buffers
-  // of K(j) and V(j-1), whose last reads finished before the barrier that
-  // ended tile j-1, while tile j is computed; S^T(j+1) is issued in the same
-  // basic block as the softmax of tile j, so MFMA and VALU work overlap.
+  // ---- main loop: two tiles per trip, ping-pong S and P registers ---------
+  // Step j: S^T(j) and P_{j-1} are ready.  K(j+2) and V(j) are loaded into the
+  // buffers of K(j) and V(j-2), whose last reads finished before the barrier
+  // that ended step j-1.  Then one basic block holds the MFMAs of S^T(j+1)
+  // and of P_{j-1} V_{j-1} and the softmax of tile j (P_j), interleaved.
+  // When the reference max must be raised (rare), P_{j-1} V_{j-1} is added
+  // first, O is rescaled and P_{j-1} cleared, so the block adds zeros.
   // (the parity of j, and so every LDS buffer offset, is a compile-time constant)
-  auto step = [&](auto parity, int j, f32x16 (&Scur)[2], f32x16 (&Snxt)[2]) {
+  auto step = [&](auto parity, int j, f32x16 (&Scur)[2], f32x16 (&Snxt)[2],
+                  u32x4 (&Pprev)[4], u32x4 (&Pcur)[4]) {
     constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
     const int kb = kb0 + j * kBlockN;
     mask_tile(Scur, kb);
-    update_max(Scur);
+    update_max(Scur, [&] {
+      pv(nxt, Pprev);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Pprev[i] = u32x4{0u, 0u, 0u, 0u};
+    });
     if (j + 2 < ntiles) fetch(krs, k_src, k_lds_addr + cur * TILE_BYTES, kb + 2 * kBlockN);
-    if (j + 1 < ntiles) fetch(vrs, v_src, v_lds_addr + nxt * TILE_BYTES, kb + kBlockN);
+    fetch(vrs, v_src, v_lds_addr + cur * TILE_BYTES, kb);
     qk(nxt, Snxt);
-    softmax(Scur, pf);
-    pv(cur, pf);
+    pv(nxt, Pprev);
+    softmax(Scur, Pcur);
+    interleave_hint();
     lds_load_wait();
     __syncthreads();
   };
   for (int j = 0; j < ntiles; j += 2) {
-    step(std::integral_constant<int, 0>{}, j, s0, s1);
-    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1, s1, s0);
+    step(std::integral_constant<int, 0>{}, j, s0, s1, p1, p0);
+    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1, s1, s0, p0, p1);
+  }
+  // the last tile's P V
+  if (ntiles > 0) {
+    if ((ntiles - 1) & 1) pv(1, p1); else pv(0, p0);
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2 ------------
