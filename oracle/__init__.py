@@ -21,13 +21,15 @@ Sources (pages on the subject, cited by title and section):
     row max m and normaliser l and reproduces the global softmax exactly.
   * "flash-attention" configuration skill page, sec. 3.2-3.5 and appendix
     (PagedAttention, FlashDecoding / Split-KV, GQA/MQA, continuous batching)
-    -- argument shapes, causal / window_size, cu_seqlens, block_table, GQA.
+    -- argument shapes, causal / window_size, cu_seqlens, block_table, GQA,
+    and k_new / v_new appended to a KV cache of cache_seqlens tokens.
 
 Readings where the pages are silent (each listed in the design doc):
   causal alignment is bottom-right; window bounds are inclusive; -1 means an
   unbounded window side; query head h uses KV head h // (Hq // Hkv); LSE is the
   natural-log log-sum-exp of the scaled scores; a row with no visible key has
-  O = 0 and LSE = -inf.
+  O = 0 and LSE = -inf; new K/V rows are appended at positions
+  cache_seqlens[b] + i.
 
 Inputs are numpy arrays; a uint16 array is taken as bfloat16 bit patterns
 (numpy has no bfloat16 type) and converted exactly to float64.
@@ -45,6 +47,8 @@ from .attention import (
     attention_varlen_ref,
     gather_paged,
     decode_paged_ref,
+    append_paged_ref,
+    attention_kvcache_ref,
     decode_split_partials_ref,
     merge_partials_ref,
     online_softmax_ref,
@@ -58,6 +62,8 @@ __all__ = [
     "attention_varlen_ref",
     "gather_paged",
     "decode_paged_ref",
+    "append_paged_ref",
+    "attention_kvcache_ref",
     "decode_split_partials_ref",
     "merge_partials_ref",
     "online_softmax_ref",

@@ -190,6 +190,63 @@ def decode_paged_ref(q, k_cache, v_cache, block_table, cache_seqlens, page_size,
     return O, LSE
 
 
+def append_paged_ref(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, page_size):
+    """Write the K/V rows of new tokens into a paged cache ("flash-attention"
+    skill page, sec. 3.5: k_new / v_new passed with cache_seqlens, each
+    request's current cache length; appendix on PagedAttention for the page
+    layout).  Reading taken where the page is silent: new token i of request b
+    goes to sequence position cache_seqlens[b] + i, i.e. page
+    block_table[b][pos // page_size], slot pos % page_size.
+
+    k_new, v_new: (B, L_new, Hkv, d).  Returns new cache arrays; the inputs are
+    not modified.
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    B, Ln = k_new.shape[:2]
+    for b in range(B):
+        pos = int(cache_seqlens[b]) + np.arange(Ln, dtype=np.int64)
+        pages = np.asarray(block_table[b], dtype=np.int64)[pos // page_size]
+        kc[pages, pos % page_size] = k_new[b]
+        vc[pages, pos % page_size] = v_new[b]
+    return kc, vc
+
+
+def attention_kvcache_ref(q, k_cache, v_cache, block_table, cache_seqlens, page_size,
+                          k_new=None, v_new=None, softmax_scale=None, causal=True,
+                          window=(-1, -1)):
+    """Attention of several new query tokens over a paged KV cache (chunked
+    prefill; "flash-attention" skill page, sec. 3.5 and the appendix on
+    PagedAttention).  When k_new / v_new are given they are first appended at
+    positions cache_seqlens[b] .. cache_seqlens[b] + Lq - 1 (append_paged_ref);
+    request b then has n_b = cache_seqlens[b] (+ Lq when appending) keys, and
+    its Lq query rows sit at the last Lq positions (bottom-right alignment, as
+    for every Lq != Lk case here).
+
+    q: (B, Lq, Hq, d).  Returns O (B, Lq, Hq, d), LSE (B, Hq, Lq) and the
+    caches after the append (the given arrays when nothing is appended).
+    """
+    q = _f64(q)
+    B, Lq, Hq, d = q.shape
+    if k_new is not None:
+        assert k_new.shape[1] == Lq and v_new.shape[1] == Lq
+        k_cache, v_cache = append_paged_ref(k_cache, v_cache, k_new, v_new, block_table,
+                                            cache_seqlens, page_size)
+        extra = Lq
+    else:
+        extra = 0
+    O = np.zeros((B, Lq, Hq, d))
+    LSE = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        n = int(cache_seqlens[b]) + extra
+        kk = _f64(gather_paged(k_cache, block_table[b], n, page_size))[None]
+        vv = _f64(gather_paged(v_cache, block_table[b], n, page_size))[None]
+        o, lse = attention_ref(q[b:b + 1], kk, vv, softmax_scale, causal, window)
+        O[b] = o[0]
+        LSE[b] = lse[0]
+    return O, LSE, k_cache, v_cache
+
+
 def decode_split_partials_ref(q_row, k, v, scale, split_tokens, lo=0):
     """Split-KV partial results for one decode query row ("flash-attention"
     skill page, appendix on FlashDecoding / Split-KV: several workers take

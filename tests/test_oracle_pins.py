@@ -376,6 +376,152 @@ def test_brute_force_varlen_and_paged():
         assert np.abs(O[b] - Ob[0]).max() < 1e-12 and np.abs(LSE[b] - LSEb[0, :, 0]).max() < 1e-12
 
 
+# ------------------------------------------- KV cache: append + chunked prefill
+def brute_force_kvcache(q, kc, vc, table, lens, ps, k_new, v_new, scale, causal, wl, wr):
+    """Pure-Python loops: new rows written slot by slot at position lens[b] + i,
+    then every (b, h, i) attends over the request's positions through the page
+    table, query row i sitting at position i + n - Lq."""
+    kc, vc = kc.copy(), vc.copy()
+    B, Lq, Hq, d = q.shape
+    Hkv = kc.shape[2]
+    G = Hq // Hkv
+    if k_new is not None:
+        for b in range(B):
+            for i in range(Lq):
+                pos = int(lens[b]) + i
+                pg, sl = int(table[b][pos // ps]), pos % ps
+                for g in range(Hkv):
+                    for t in range(d):
+                        kc[pg, sl, g, t] = k_new[b, i, g, t]
+                        vc[pg, sl, g, t] = v_new[b, i, g, t]
+    O = np.zeros((B, Lq, Hq, d))
+    LSE = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        n = int(lens[b]) + (Lq if k_new is not None else 0)
+        for h in range(Hq):
+            g = h // G
+            for i in range(Lq):
+                p_i = i + n - Lq
+                keys = [j for j in range(n)
+                        if (not causal or j <= p_i) and (wl < 0 or j >= p_i - wl)
+                        and (wr < 0 or j <= p_i + wr)]
+                if not keys:
+                    LSE[b, h, i] = -math.inf
+                    continue
+                row = {j: (int(table[b][j // ps]), j % ps) for j in keys}
+                s = {j: scale * math.fsum(q[b, i, h, t] * kc[row[j][0], row[j][1], g, t] for t in range(d))
+                     for j in keys}
+                m = max(s.values())
+                e = {j: math.exp(s[j] - m) for j in keys}
+                l = math.fsum(e.values())
+                for t in range(d):
+                    O[b, i, h, t] = math.fsum(e[j] * vc[row[j][0], row[j][1], g, t] for j in keys) / l
+                LSE[b, h, i] = m + math.log(l)
+    return O, LSE, kc, vc
+
+
+def _kvcache_case(seed, B=2, Lq=3, Hq=4, Hkv=2, d=3, ps=2, lens=(5, 2), npages=6):
+    rng = np.random.default_rng(seed)
+    pool = B * npages + 2
+    kc = rng.standard_normal((pool, ps, Hkv, d))
+    vc = rng.standard_normal((pool, ps, Hkv, d))
+    table = rng.permutation(pool)[:B * npages].reshape(B, npages)
+    q = rng.standard_normal((B, Lq, Hq, d))
+    kn = rng.standard_normal((B, Lq, Hkv, d))
+    vn = rng.standard_normal((B, Lq, Hkv, d))
+    return q, kc, vc, table, np.array(lens), ps, kn, vn
+
+
+@pytest.mark.parametrize("append", [False, True])
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (True, (2, 0)), (False, (-1, -1)),
+                                           (False, (1, 1))])
+def test_brute_force_kvcache(append, causal, window):
+    q, kc, vc, table, lens, ps, kn, vn = _kvcache_case(21)
+    if not append:
+        kn = vn = None
+        lens = np.array([7, 4])
+    O, LSE, kc2, vc2 = oracle.attention_kvcache_ref(q, kc, vc, table, lens, ps, kn, vn, 0.6, causal, window)
+    Ob, LSEb, kcb, vcb = brute_force_kvcache(q, kc, vc, table, lens, ps, kn, vn, 0.6, causal, *window)
+    fin = np.isfinite(LSEb)
+    assert np.array_equal(fin, np.isfinite(LSE))
+    assert np.abs(LSE[fin] - LSEb[fin]).max() < 1e-12
+    assert np.abs(O - Ob).max() < 1e-12
+    assert np.array_equal(kc2, kcb) and np.array_equal(vc2, vcb)
+
+
+def test_kvcache_equals_contiguous_attention():
+    rng = np.random.default_rng(22)
+    B, L0, Lq, Hq, Hkv, d, ps = 2, 13, 6, 4, 2, 8, 4
+    k_all, v_all = rand(B, L0 + Lq, Hkv, d), rand(B, L0 + Lq, Hkv, d)
+    q = rand(B, Lq, Hq, d)
+    # cache holds the first L0 tokens; pages for the appended ones exist but hold NaN
+    kc, vc, table = _paged_from_contiguous(k_all[:, :L0], v_all[:, :L0], ps, rng, pool_extra=12)
+    npg = -(-(L0 + Lq) // ps)
+    free = [p for p in range(kc.shape[0]) if p not in set(table.ravel())]
+    table = np.concatenate([table, np.array(free[:B * (npg - table.shape[1])]).reshape(B, -1)], 1)
+    lens = np.full(B, L0)
+    for causal, window in [(True, (-1, -1)), (True, (5, 0)), (False, (-1, -1))]:
+        O, LSE, kc2, vc2 = oracle.attention_kvcache_ref(q, kc, vc, table, lens, ps, k_all[:, L0:],
+                                                        v_all[:, L0:], 0.35, causal, window)
+        Of, LSEf = oracle.attention_ref(q, k_all, v_all, 0.35, causal, window)
+        assert np.abs(O - Of).max() < 1e-13 and np.abs(LSE - LSEf).max() < 1e-13
+    # the appended rows are where positions L0 .. L0+Lq-1 say
+    for b in range(B):
+        assert np.array_equal(oracle.gather_paged(kc2, table[b], L0 + Lq, ps), k_all[b])
+    # without new rows: the queries sit at the last Lq cached positions
+    O, LSE, kc3, _ = oracle.attention_kvcache_ref(q, kc2, vc2, table, np.full(B, L0 + Lq), ps,
+                                                  None, None, 0.35, True)
+    Of, LSEf = oracle.attention_ref(q, k_all, v_all, 0.35, True)
+    assert kc3 is kc2
+    assert np.abs(O - Of).max() < 1e-13 and np.abs(LSE - LSEf).max() < 1e-13
+
+
+def test_kvcache_single_query_row_equals_decode():
+    rng = np.random.default_rng(23)
+    B, L, Hq, Hkv, d, ps = 3, 17, 4, 1, 8, 4
+    k, v = rand(B, L, Hkv, d), rand(B, L, Hkv, d)
+    kc, vc, table = _paged_from_contiguous(k, v, ps, rng)
+    q = rand(B, 1, Hq, d)
+    lens = np.array([17, 9, 1])
+    O, LSE, _, _ = oracle.attention_kvcache_ref(q, kc, vc, table, lens, ps, None, None, 0.5, True)
+    Od, LSEd = oracle.decode_paged_ref(q, kc, vc, table, lens, ps, 0.5)
+    assert np.abs(O - Od).max() < 1e-13 and np.abs(LSE[:, :, 0] - LSEd).max() < 1e-13
+
+
+def test_append_touches_only_the_new_slots():
+    q, kc, vc, table, lens, ps, kn, vn = _kvcache_case(24)
+    kc2, vc2 = oracle.append_paged_ref(kc, vc, kn, vn, table, lens, ps)
+    changed = ~np.all(kc2 == kc, axis=(2, 3))
+    expect = np.zeros_like(changed)
+    for b in range(len(lens)):
+        for i in range(kn.shape[1]):
+            pos = lens[b] + i
+            expect[table[b][pos // ps], pos % ps] = True
+    assert np.array_equal(changed, expect)
+    assert np.array_equal(~np.all(vc2 == vc, axis=(2, 3)), expect)
+    assert not np.shares_memory(kc2, kc)
+
+
+def test_kvcache_planted_mistakes_are_caught(monkeypatch):
+    q, kc, vc, table, lens, ps, kn, vn = _kvcache_case(25)
+    Ob, LSEb, _, _ = brute_force_kvcache(q, kc, vc, table, lens, ps, kn, vn, 0.6, True, -1, -1)
+    orig_append, orig_gather = oracle_attention.append_paged_ref, oracle_attention.gather_paged
+
+    def append_off_by_one(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, page_size):
+        return orig_append(k_cache, v_cache, k_new, v_new, block_table, np.asarray(cache_seqlens) - 1, page_size)
+
+    def gather_shifted(cache, block_table_row, length, page_size):
+        j = np.arange(length, dtype=np.int64) + 1
+        return cache[np.asarray(block_table_row, dtype=np.int64)[j // page_size], j % page_size]
+
+    for name, mut in [("append_paged_ref", append_off_by_one), ("gather_paged", gather_shifted)]:
+        monkeypatch.setattr(oracle_attention, name, mut)
+        O, LSE, _, _ = oracle_attention.attention_kvcache_ref(q, kc, vc, table, lens, ps, kn, vn, 0.6, True)
+        assert np.abs(O - Ob).max() > 1e-3, name
+        monkeypatch.setattr(oracle_attention, "append_paged_ref", orig_append)
+        monkeypatch.setattr(oracle_attention, "gather_paged", orig_gather)
+
+
 # ---------------------------------------------------------- planted mistakes
 def _pin_suite(attn):
     """A few pins rerun against a (possibly mutated) attention function; returns
