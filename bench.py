@@ -12,7 +12,8 @@ time: the GPU raises its engine clock only after some milliseconds of
 sustained load, and without this the first tens of milliseconds (the whole
 timed region at small K) run at a lower clock.
 The other workloads (long-context GQA prefill, paged decode, varlen window
-prefill, the small dense case) are timed in the same run and reported under
+prefill, the small dense case, and a chunk of 512 new tokens appended to and
+attending over a paged cache) are timed in the same run and reported under
 "workloads".  One JSON line is printed.
 
 "roofline" covers the dominant kernel (the prefill kernel on the main
@@ -266,6 +267,21 @@ def bench_others(fa, args):
         wl["varlen_window"] = {"ms": round(ms, 4), "TFLOP/s": round(f5 / ms / 1e9, 2),
                                "frac_mfma": round(f5 / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": f5}
         del a, w5
+
+        w6 = workloads.chunked_prefill()
+        q6, kc6, vc6 = w6.q.cuda(), w6.k_cache.cuda(), w6.v_cache.cuda()
+        kn6, vn6 = w6.k_new.cuda(), w6.v_new.cuda()
+        bt6 = torch.from_numpy(w6.block_table).cuda()
+        sl6 = torch.from_numpy(w6.cache_seqlens).cuda()
+        Lq6, Hq6, d6 = w6.q.shape[1], w6.q.shape[2], w6.q.shape[3]
+        f6 = 4.0 * d6 * Hq6 * sum(visible_pairs(Lq6, int(n) + Lq6, True, -1, -1) for n in w6.cache_seqlens)
+        # a step appends the chunk's K/V rows (same values each call) and attends over the cache
+        ms = time_calls(lambda: fa.fa_fwd_kvcache(q6, kc6, vc6, bt6, sl6, kn6, vn6, w6.scale, True),
+                        args.steps, args.warmup, args.prewarm_ms)
+        wl["chunked_prefill"] = {"ms": round(ms, 4), "TFLOP/s": round(f6 / ms / 1e9, 2),
+                                 "frac_mfma": round(f6 / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": f6,
+                                 "kernels": "kvcache_append + prefill_fwd<paged>"}
+        del q6, kc6, vc6, kn6, vn6, w6
 
     w4 = workloads.paged_decode()
     qd, kc, vc = w4.q.cuda(), w4.k_cache.cuda(), w4.v_cache.cuda()

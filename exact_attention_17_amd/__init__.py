@@ -40,6 +40,9 @@ _EXPORTS = {
                         + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                                 ctypes.c_void_p, ctypes.c_size_t,
                                                 ctypes.c_void_p]),
+    "fa_fwd_kvcache": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 8
+                       + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                          ctypes.c_void_p]),
 }
 
 
@@ -224,6 +227,50 @@ def fa_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, softmax_sca
     return out, lse
 
 
+def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=None,
+                   softmax_scale=None, causal=True, window=(-1, -1), out=None, lse=None,
+                   return_lse=True, stream=None):
+    """Chunked prefill over a paged KV cache: q (B, Lq, Hq, d) attends to each
+    request's cache_seqlens[b] cached keys, after k_new / v_new (B, Lq, Hkv, d),
+    if given, are written into the caches at positions cache_seqlens[b] + i
+    (in place; cache_seqlens is not changed).  Caches [num_pages, page_size,
+    Hkv, d] with page_size a multiple of 16.  Returns O (B, Lq, Hq, d) and LSE
+    (B, Hq, Lq)."""
+    torch = _torch()
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, Lq, Hq, d = q.shape
+    num_pages, page_size, Hkv, dk = k_cache.shape
+    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [num_pages, page_size, Hkv, d]")
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        _need(k_new, "k_new", torch.bfloat16, 4)
+        _need(v_new, "v_new", torch.bfloat16, 4)
+        if tuple(k_new.shape) != (B, Lq, Hkv, d) or tuple(v_new.shape) != (B, Lq, Hkv, d):
+            raise ValueError("k_new / v_new must be (B, Lq, Hkv, d)")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    wl, wr = window
+    st = lib.fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                            _ptr(block_table), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
+                            B, Lq, Hq, Hkv, d, num_pages, page_size, block_table.shape[1],
+                            scale, int(bool(causal)), int(wl), int(wr), _stream(stream))
+    _check("fa_fwd_kvcache", st)
+    return out, lse
+
+
 __all__ = ["fa_fwd", "fa_fwd_varlen", "fa_decode_paged", "fa_decode_paged_workspace_size",
+           "fa_fwd_kvcache",
            "load_library", "exported_symbols", "cu_seqlens_from_lengths",
            "lengths_from_cu_seqlens", "FAError", "LIB_PATH"]

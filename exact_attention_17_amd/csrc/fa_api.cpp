@@ -92,7 +92,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   // KV groups per XCD chunk: about one XCD's worth of resident workgroups
   p.chunk_groups = (int)std::max<int64_t>(1, fa::kPrefillSlotsPerXcd / ((int64_t)p.group * p.num_q_tiles));
   if ((int64_t)p.num_q_tiles * B * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
-  hipError_t e = fa::launch_prefill(p, d, false, static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_prefill(p, d, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -133,7 +133,77 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   p.num_q_tiles = total_q / fa::kBlockM + B;
   p.xcd_groups = xcd_groups(Hkv);
   if ((int64_t)p.num_q_tiles * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
-  hipError_t e = fa::launch_prefill(p, d, true, static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_prefill(p, d, 1, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
+                         const void* k_new, const void* v_new,
+                         const int* block_table, const int* cache_seqlens,
+                         void* o, float* lse, int B, int Lq, int Hq, int Hkv, int d,
+                         int num_pages, int page_size, int max_blocks_per_seq,
+                         float softmax_scale, int causal, int window_left, int window_right,
+                         void* stream) {
+  fa_status st = check_common(Hq, Hkv, d, softmax_scale, causal, window_left, window_right);
+  if (st != FA_OK) return st;
+  if ((st = check_tensors(q, k_cache, v_cache, o, lse)) != FA_OK) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return FA_ERR_INVALID_ARG;
+  if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) return FA_ERR_INVALID_ARG;
+  if (!block_table || !cache_seqlens || !aligned(block_table, 4) || !aligned(cache_seqlens, 4))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || Lq < 0 || num_pages < 1 || max_blocks_per_seq < 1 || page_size < 1)
+    return FA_ERR_INVALID_ARG;
+  if (page_size % 16 != 0) return FA_ERR_UNSUPPORTED;
+  // one page of one KV head is addressed with 32-bit byte offsets, with room
+  // for the out-of-range marker; queries per request likewise
+  if ((int64_t)page_size * Hkv * d * 2 >= ((int64_t)1 << 30)) return FA_ERR_INVALID_ARG;
+  if ((int64_t)Lq * Hq * d >= kMaxBatchElems) return FA_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * page_size >= ((int64_t)1 << 30)) return FA_ERR_INVALID_ARG;
+  if (Lq == 0) return FA_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (k_new) {
+    fa::AppendParams a = {};
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.k_cache = static_cast<uint16_t*>(k_cache);
+    a.v_cache = static_cast<uint16_t*>(v_cache);
+    a.block_table = block_table;
+    a.cache_seqlens = cache_seqlens;
+    a.B = B; a.L_new = Lq; a.Hkv = Hkv; a.d = d;
+    a.page_size = page_size; a.max_blocks = max_blocks_per_seq;
+    if (B > 65535) return FA_ERR_INVALID_ARG;   // append grid (Lq, B)
+    if (fa::launch_append(a, s) != hipSuccess) return FA_ERR_HIP;
+  }
+
+  fa::PrefillParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B; p.Lq = Lq; p.Lk = 0;   // per request: cache_seqlens[b] + append_len
+  p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.q_tok_stride = (int64_t)Hq * d;
+  p.k_tok_stride = (int64_t)Hkv * d;
+  p.q_batch_stride = (int64_t)Lq * Hq * d;
+  p.k_batch_stride = 0;
+  p.lse_seq_stride = Lq;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
+  p.xcd_groups = xcd_groups(B * Hkv);
+  p.chunk_groups = (int)std::max<int64_t>(1, fa::kPrefillSlotsPerXcd / ((int64_t)p.group * p.num_q_tiles));
+  if ((int64_t)p.num_q_tiles * B * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
+  p.block_table = block_table;
+  p.cache_seqlens = cache_seqlens;
+  p.page_size = page_size;
+  p.max_blocks = max_blocks_per_seq;
+  p.append_len = k_new ? Lq : 0;
+  p.page_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == page_size) p.page_shift = sh;
+  hipError_t e = fa::launch_prefill(p, d, 2, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

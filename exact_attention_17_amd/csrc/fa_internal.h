@@ -40,6 +40,23 @@ struct PrefillParams {
   int num_q_tiles;         // dense: ceil(Lq / kBlockM); varlen: total tile slots
   int xcd_groups;          // >0: XCD-aware work mapping with this many KV groups
   int chunk_groups;        // KV groups an XCD works on together (dense mapping)
+  // paged KV cache (chunked prefill): k/v are the page pools
+  // [num_pages][page_size][Hkv][d]; request b has cache_seqlens[b] + append_len keys
+  const int* block_table;  // [B][max_blocks]
+  const int* cache_seqlens;
+  int page_size, max_blocks, append_len;
+  int page_shift;          // log2(page_size) when a power of two, else -1
+};
+
+// Copy new tokens' K/V rows into a paged cache (see fa_fwd_kvcache).
+struct AppendParams {
+  const uint16_t* k_new;   // (B, L_new, Hkv, d)
+  const uint16_t* v_new;
+  uint16_t* k_cache;       // [num_pages][page_size][Hkv][d]
+  uint16_t* v_cache;
+  const int* block_table;
+  const int* cache_seqlens;
+  int B, L_new, Hkv, d, page_size, max_blocks;
 };
 
 struct DecodeParams {
@@ -58,7 +75,9 @@ struct DecodeParams {
   int win_left;
 };
 
-hipError_t launch_prefill(const PrefillParams& p, int d, bool varlen, hipStream_t stream);
+// mode: 0 dense, 1 varlen, 2 paged KV cache
+hipError_t launch_prefill(const PrefillParams& p, int d, int mode, hipStream_t stream);
+hipError_t launch_append(const AppendParams& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, int rows, hipStream_t stream);
 
 }  // namespace fa

@@ -103,9 +103,12 @@ FA_DEV uint32_t lds_address(const void* p) {
 // lds_base + 16 l (soffset and lds_base must be wave-uniform; lds_base goes
 // in M0).  The range check applies to voffset + soffset: out-of-range lanes
 // store zeros.  The compiler does not track these loads, so lds_load_wait()
-// must run before the data is read.
+// must run before the data is read.  Nor does it see the instruction's
+// hazards: an SGPR operand written by a VALU op (v_readfirstlane) needs 5 wait
+// states before a VMEM read, and M0 one before an LDS-destination load, so 5
+// are inserted here.
 FA_DEV void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset, uint32_t lds_base) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(lds_base) : "memory");
 }
 FA_DEV void lds_load_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -10,7 +10,10 @@
 //   sec. 1.2 and 4.2).  Q is split into row blocks and K/V into column blocks
 //   held on chip (the "FlashAttention" concept page, tiling strategy).
 //   Causal and sliding-window masks, GQA broadcast and packed varlen batches
-//   follow the configuration skill page (sec. 3.2-3.4, GQA appendix).
+//   follow the configuration skill page (sec. 3.2-3.4, GQA appendix).  The
+//   paged mode reads K/V of several new query rows per request from a paged
+//   KV cache through its block table (skill page sec. 3.5 and the appendix on
+//   PagedAttention), after an optional append of the new rows.
 //
 // Mapping onto CDNA4 (our design, not the pages'):
 //   * A workgroup is 4 wave64s and owns 128 query rows of one (batch, head);
@@ -154,9 +157,12 @@ __device__ __forceinline__ WorkItem map_work_varlen(const PrefillParams& p, int 
 
 }  // namespace
 
-template <int D, bool VARLEN>
+// MODE 0: dense (B, L, H, d); 1: packed varlen; 2: queries dense (B, Lq, Hq, d),
+// keys from a paged KV cache.
+template <int D, int MODE>
 __global__ __launch_bounds__(kPrefillThreads, 2)
 void prefill_fwd_kernel(PrefillParams p) {
+  constexpr bool VARLEN = MODE == 1, PAGED = MODE == 2;
   constexpr int KSTEPS = D / 16;                 // QK^T MFMA steps over d
   constexpr int DBLK = D / 32;                   // 32-row blocks of O^T
   constexpr int KCH = D / 8;                     // 16-byte chunks per row
@@ -169,11 +175,14 @@ void prefill_fwd_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2 * Lds<D>::kTile];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same in all lanes: keep it (and everything derived
+  // from it, such as load offsets) in scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hi = lane >> 5;
   const int i16 = lane & 15, g16 = lane >> 4;
 
-  const WorkItem w = VARLEN ? map_work_varlen(p, blockIdx.x) : map_work_dense(p, blockIdx.x);
+  WorkItem w = VARLEN ? map_work_varlen(p, blockIdx.x) : map_work_dense(p, blockIdx.x);
+  if (PAGED) w.Lk = p.cache_seqlens[w.b] + p.append_len;
   if (!w.valid) return;
   const int Lq = w.Lq, Lk = w.Lk;
   const int kvh = w.h / p.group;
@@ -193,8 +202,10 @@ void prefill_fwd_kernel(PrefillParams p) {
   } else {
     qg = p.q + (int64_t)w.b * p.q_batch_stride + (int64_t)w.h * D;
     og = p.o + (int64_t)w.b * p.q_batch_stride + (int64_t)w.h * D;
-    kg = p.k + (int64_t)w.b * p.k_batch_stride + (int64_t)kvh * D;
-    vg = p.v + (int64_t)w.b * p.k_batch_stride + (int64_t)kvh * D;
+    // paged: the pools, offset to this KV head; rows are addressed per page
+    const int64_t kb_off = PAGED ? 0 : (int64_t)w.b * p.k_batch_stride;
+    kg = p.k + kb_off + (int64_t)kvh * D;
+    vg = p.v + kb_off + (int64_t)kvh * D;
     if (p.lse) lseg = p.lse + ((int64_t)w.b * p.Hq + w.h) * p.lse_seq_stride;
   }
 
@@ -250,11 +261,58 @@ void prefill_fwd_kernel(PrefillParams p) {
   }
   const uint32_t k_lds_addr = lds_address(k_lds), v_lds_addr = lds_address(v_lds);
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
-  auto fetch = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t src, uint32_t dst, int kb) {
+  // Paged mode: the 4 * RPI rows of load instruction i lie in one page (page
+  // sizes are multiples of 16), whose id is one scalar load; the descriptor
+  // spans that page's rows of this KV head, so the scalar offset is the row in
+  // the page.  Keys at or past Lk get an out-of-range lane offset and load as
+  // zeros; a key past the last used page reads page 0's range, never an
+  // unused block-table entry.
+  const int* bt_row = PAGED ? p.block_table + (int64_t)w.b * p.max_blocks : nullptr;
+  const int64_t page_elems = PAGED ? (int64_t)p.page_size * p.k_tok_stride : 0;
+  const uint32_t page_bytes = PAGED ? (uint32_t)((p.page_size - 1) * k_row_bytes + D * 2) : 0u;
+  const uint32_t lane_row = (uint32_t)(lane / KCH);
+  const uint32_t k_src_pg = k_src - (uint32_t)(wave * RPI) * k_row_bytes;   // row part of the lane
+  const uint32_t v_src_pg = v_src - (uint32_t)(wave * RPI) * k_row_bytes;
+  // Page ids of the LOADS row groups this wave loads for the tile at kb, read
+  // together (scalar loads) ahead of the loads that need them.  The index is
+  // clamped to the last used page: rows past Lk load as zeros in any case.
+  const int last_pidx = PAGED && Lk > 0 ? (Lk - 1) / p.page_size : 0;
+  // read through the constant address space: scalar loads (the table is not
+  // written by this kernel), counted apart from the direct-to-LDS loads
+  const __attribute__((address_space(4))) int* bt_const = (const __attribute__((address_space(4))) int*)bt_row;
+  struct PageIds { int pg[LOADS]; };
+  auto page_ids = [&](int kb) {
+    PageIds r;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const uint32_t soff = (uint32_t)(kb + 4 * i * RPI) * k_row_bytes;
-      lds_load16(rs, src, (uint32_t)__builtin_amdgcn_readfirstlane(soff), dst + wave_lds + 4096u * i);
+      if (PAGED) {
+        const int key0 = kb + (4 * i + wave) * RPI;
+        const int pidx = p.page_shift >= 0 ? key0 >> p.page_shift : key0 / p.page_size;
+        r.pg[i] = bt_const[min(pidx, last_pidx)];
+      } else {
+        r.pg[i] = 0;
+      }
+    }
+    return r;
+  };
+  // src / src_pg: the lane's byte offset for K or V; gbase: that tensor's base.
+  auto fetch = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t src, uint32_t src_pg,
+                   const uint16_t* gbase, uint32_t dst, int kb, const PageIds& ids) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      if (!PAGED) {
+        const uint32_t soff = (uint32_t)(kb + 4 * i * RPI) * k_row_bytes;
+        lds_load16(rs, src, (uint32_t)__builtin_amdgcn_readfirstlane(soff), dst + wave_lds + 4096u * i);
+      } else {
+        const int key0 = kb + (4 * i + wave) * RPI;                  // wave-uniform
+        const int pidx = p.page_shift >= 0 ? key0 >> p.page_shift : key0 / p.page_size;
+        const int prow = key0 - pidx * p.page_size;
+        const uint16_t* base = gbase + (int64_t)ids.pg[i] * page_elems;
+        const uint32_t soff = (uint32_t)prow * k_row_bytes;
+        const uint32_t off = src_pg | ((uint32_t)key0 + lane_row >= (uint32_t)Lk ? kOob : 0u);
+        lds_load16(make_rsrc(base, page_bytes), off, (uint32_t)__builtin_amdgcn_readfirstlane(soff),
+                   dst + wave_lds + 4096u * i);
+      }
     }
   };
 
@@ -385,8 +443,9 @@ void prefill_fwd_kernel(PrefillParams p) {
   // (step 0 multiplies V buffer 1 by P = 0: it must hold finite values)
   const int kb0 = kt_begin * kBlockN;
   if (ntiles > 0) {
-    fetch(krs, k_src, k_lds_addr, kb0);
-    if (ntiles > 1) fetch(krs, k_src, k_lds_addr + TILE_BYTES, kb0 + kBlockN);
+    const PageIds i0 = page_ids(kb0), i1 = page_ids(kb0 + kBlockN);
+    fetch(krs, k_src, k_src_pg, kg, k_lds_addr, kb0, i0);
+    if (ntiles > 1) fetch(krs, k_src, k_src_pg, kg, k_lds_addr + TILE_BYTES, kb0 + kBlockN, i1);
   }
 #pragma unroll
   for (int i = 0; i < TILE_BYTES / 16 / kPrefillThreads; ++i)
@@ -422,8 +481,9 @@ void prefill_fwd_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) Pprev[i] = u32x4{0u, 0u, 0u, 0u};
     });
-    if (j + 2 < ntiles) fetch(krs, k_src, k_lds_addr + cur * TILE_BYTES, kb + 2 * kBlockN);
-    fetch(vrs, v_src, v_lds_addr + cur * TILE_BYTES, kb);
+    const PageIds ik = page_ids(kb + 2 * kBlockN), iv = page_ids(kb);
+    if (j + 2 < ntiles) fetch(krs, k_src, k_src_pg, kg, k_lds_addr + cur * TILE_BYTES, kb + 2 * kBlockN, ik);
+    fetch(vrs, v_src, v_src_pg, vg, v_lds_addr + cur * TILE_BYTES, kb, iv);
     qk(nxt, Snxt);
     pv(nxt, Pprev);
     softmax(Scur, Pcur);
@@ -460,18 +520,43 @@ void prefill_fwd_kernel(PrefillParams p) {
   }
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int d, bool varlen, hipStream_t stream) {
-  const int64_t nblocks = varlen ? (int64_t)p.num_q_tiles * p.Hq
-                                 : (int64_t)p.num_q_tiles * p.B * p.Hq;
+hipError_t launch_prefill(const PrefillParams& p, int d, int mode, hipStream_t stream) {
+  const int64_t nblocks = mode == 1 ? (int64_t)p.num_q_tiles * p.Hq
+                                    : (int64_t)p.num_q_tiles * p.B * p.Hq;
   if (nblocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)nblocks), block(kPrefillThreads);
+#define FA_PREFILL(DD, MM) hipLaunchKernelGGL((prefill_fwd_kernel<DD, MM>), grid, block, 0, stream, p)
   if (d == 128) {
-    if (varlen) hipLaunchKernelGGL((prefill_fwd_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_fwd_kernel<128, false>), grid, block, 0, stream, p);
+    if (mode == 0) FA_PREFILL(128, 0); else if (mode == 1) FA_PREFILL(128, 1); else FA_PREFILL(128, 2);
   } else {
-    if (varlen) hipLaunchKernelGGL((prefill_fwd_kernel<64, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_fwd_kernel<64, false>), grid, block, 0, stream, p);
+    if (mode == 0) FA_PREFILL(64, 0); else if (mode == 1) FA_PREFILL(64, 1); else FA_PREFILL(64, 2);
   }
+#undef FA_PREFILL
+  return hipGetLastError();
+}
+
+// One workgroup per (new token i, request b): 16-byte copies of the token's
+// K and V rows (all KV heads) into cache position cache_seqlens[b] + i.
+__global__ __launch_bounds__(256)
+void kvcache_append_kernel(AppendParams a) {
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int pos = a.cache_seqlens[b] + i;
+  const int pg = a.block_table[(int64_t)b * a.max_blocks + pos / a.page_size];
+  const int64_t row = (int64_t)a.Hkv * a.d;                  // elements per token
+  const int64_t dst = ((int64_t)pg * a.page_size + pos % a.page_size) * row;
+  const int64_t src = ((int64_t)b * a.L_new + i) * row;
+  const int chunks = (int)(row / 8);
+  for (int c = threadIdx.x; c < 2 * chunks; c += blockDim.x) {
+    const bool is_v = c >= chunks;
+    const int cc = is_v ? c - chunks : c;
+    const u32x4 val = *reinterpret_cast<const u32x4*>((is_v ? a.v_new : a.k_new) + src + 8 * cc);
+    *reinterpret_cast<u32x4*>((is_v ? a.v_cache : a.k_cache) + dst + 8 * cc) = val;
+  }
+}
+
+hipError_t launch_append(const AppendParams& a, hipStream_t stream) {
+  if (a.B <= 0 || a.L_new <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kvcache_append_kernel, dim3(a.L_new, a.B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

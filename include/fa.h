@@ -131,6 +131,40 @@ fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cach
                           float softmax_scale, int window_left, int split_tokens,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Attention of Lq new query tokens per request over a paged KV cache
+ * (chunked prefill), with an optional append of their K/V rows first
+ * (skill page sec. 3.5: k_new / v_new and cache_seqlens; appendix on
+ * PagedAttention for the cache layout).
+ *   q, o     : (B, Lq, Hq, d) bf16
+ *   k_cache, v_cache : [num_pages, page_size, Hkv, d] bf16; page_size must be
+ *       a positive multiple of 16 (else FA_ERR_UNSUPPORTED) and one page of
+ *       one cache must be < 2^30 bytes.
+ *   k_new, v_new : (B, Lq, Hkv, d) bf16, both NULL or both set.  When set,
+ *       new token i of request b is first written to sequence position
+ *       cache_seqlens[b] + i (page block_table[b][pos / page_size], slot
+ *       pos % page_size); the caches are modified in place and
+ *       cache_seqlens is not updated (the caller advances it).
+ *   block_table : device int32 [B, max_blocks_per_seq].
+ *   cache_seqlens : device int32 [B]: keys already in the cache.  Request b
+ *       attends to n_b = cache_seqlens[b] (+ Lq when appending) keys, with
+ *       n_b <= max_blocks_per_seq * page_size and the first ceil(n_b /
+ *       page_size) table entries valid (not checked on the device).
+ *   lse      : (B, Hq, Lq) float32, or NULL.
+ *   causal, window_left, window_right : as fa_fwd, with query row i at key
+ *       position i + n_b - Lq (bottom-right).
+ * Cache contents at or past a request's n_b never influence the result.
+ * The append (when requested) and the attention are enqueued on `stream` in
+ * that order.
+ */
+fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
+                         const void* k_new, const void* v_new,
+                         const int* block_table, const int* cache_seqlens,
+                         void* o, float* lse, int B, int Lq, int Hq, int Hkv, int d,
+                         int num_pages, int page_size, int max_blocks_per_seq,
+                         float softmax_scale, int causal, int window_left, int window_right,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

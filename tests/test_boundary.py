@@ -34,7 +34,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == sorted(["fa_status_string", "fa_fwd", "fa_fwd_varlen",
-                            "fa_decode_paged_workspace_size", "fa_decode_paged"])
+                            "fa_decode_paged_workspace_size", "fa_decode_paged", "fa_fwd_kvcache"])
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(fa.exported_symbols()) == names
@@ -122,6 +122,33 @@ def decode(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
+
+
+def kvcache(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, kn=P, vn=P, bt=P, sl=P, o=P, lse=P, B=2, Lq=64, Hq=8, Hkv=2, d=128,
+             pages=64, ps=16, mb=8, scale=0.1, causal=1, wl=-1, wr=-1)
+    a.update(kw)
+    return lib.fa_fwd_kvcache(a["q"], a["kc"], a["vc"], a["kn"], a["vn"], a["bt"], a["sl"], a["o"],
+                              a["lse"], a["B"], a["Lq"], a["Hq"], a["Hkv"], a["d"], a["pages"], a["ps"],
+                              a["mb"], a["scale"], a["causal"], a["wl"], a["wr"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), INVALID), (dict(vn=None), INVALID), (dict(kn=P + 8), INVALID),
+    (dict(bt=None), INVALID), (dict(sl=P + 2), INVALID), (dict(kc=None), INVALID),
+    (dict(o=P + 4), INVALID), (dict(B=0), INVALID), (dict(Lq=-1), INVALID),
+    (dict(pages=0), INVALID), (dict(mb=0), INVALID), (dict(ps=0), INVALID),
+    (dict(ps=8), UNSUPPORTED), (dict(ps=24), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(Hkv=3), INVALID), (dict(scale=float("nan")), INVALID), (dict(causal=5), INVALID),
+    (dict(wl=-3), INVALID), (dict(ps=1 << 16, Hkv=64), INVALID), (dict(mb=1 << 26, ps=16), INVALID),
+])
+def test_kvcache_rejects(lib, kw, code):
+    assert kvcache(lib, **kw) == code
+
+
+def test_kvcache_no_query_rows_is_a_no_op(lib):
+    assert kvcache(lib, Lq=0) == OK
+    assert kvcache(lib, Lq=0, kn=None, vn=None) == OK
 
 
 def _golden_cu():

@@ -211,3 +211,56 @@ def test_full_varlen_window(fa):
             O, LSE = oracle.attention_rows_ref(qb[None, s:s + L], kb[None, s:s + L], vb[None, s:s + L],
                                                0, h, rows, w.scale, w.causal, w.window)
             check(f"{w.name} seq{b} h{h}", o[s + rows, h], lse[h, s + rows], O, LSE)
+
+
+# ------------------------------------------- chunked prefill over a paged cache
+def run_kvcache(fa, w):
+    """fa_fwd_kvcache on device copies; returns O, LSE and the caches after it."""
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    kn = dev(w.k_new) if w.k_new is not None else None
+    vn = dev(w.v_new) if w.v_new is not None else None
+    o, lse = fa.fa_fwd_kvcache(dev(w.q), kc, vc, dev(torch.from_numpy(w.block_table)),
+                               dev(torch.from_numpy(w.cache_seqlens)), kn, vn, w.scale, w.causal,
+                               w.window)
+    torch.cuda.synchronize()
+    return o, lse, kc.cpu(), vc.cpu()
+
+
+def kvcache_ref(w):
+    kn = bits(w.k_new) if w.k_new is not None else None
+    vn = bits(w.v_new) if w.v_new is not None else None
+    return oracle.attention_kvcache_ref(bits(w.q), bits(w.k_cache), bits(w.v_cache), w.block_table,
+                                        w.cache_seqlens, w.page_size, kn, vn, w.scale, w.causal,
+                                        w.window)
+
+
+# (cached lengths, Lq, Hq, Hkv, d, page_size, append, causal, window)
+KVCACHE_CASES = [
+    ([300, 17, 1000], 70, 8, 2, 128, 16, True, True, (-1, -1)),
+    ([0, 129, 64], 130, 4, 4, 64, 16, True, True, (-1, -1)),      # an empty cache
+    ([513, 200], 1, 8, 1, 128, 32, False, True, (-1, -1)),        # one query row, no append
+    ([1000, 300], 257, 8, 2, 128, 16, False, True, (100, 0)),     # keys fewer than queries
+    ([77, 400], 33, 6, 3, 64, 48, True, False, (-1, -1)),         # non-causal, 48-token pages
+    ([2000, 5], 300, 8, 8, 128, 16, True, True, (64, 0)),         # window across the append
+    ([0, 0], 5, 2, 1, 128, 16, False, True, (-1, -1)),            # nothing to attend to
+]
+
+
+@pytest.mark.parametrize("case", KVCACHE_CASES,
+                         ids=lambda c: f"n{len(c[0])}-lq{c[1]}-h{c[2]}-kv{c[3]}-d{c[4]}-p{c[5]}-a{int(c[6])}-c{int(c[7])}-w{c[8][0]}")
+def test_kvcache_sweep(fa, case):
+    lens, Lq, Hq, Hkv, d, ps, append, causal, window = case
+    w = workloads.random_kvcache(600 + sum(lens) + Lq, lens, Lq, Hq, Hkv, d, ps, append, causal, window)
+    o, lse, kc, vc = run_kvcache(fa, w)
+    O, LSE, kc_ref, vc_ref = kvcache_ref(w)
+    check(f"kvcache{case}", o, lse, O, LSE)
+    # the append wrote exactly the new rows, bit for bit, and nothing else
+    assert np.array_equal(bits(kc), kc_ref) and np.array_equal(bits(vc), vc_ref)
+
+
+def test_full_chunked_prefill(fa):
+    w = workloads.chunked_prefill()
+    o, lse, kc, vc = run_kvcache(fa, w)
+    O, LSE, kc_ref, vc_ref = kvcache_ref(w)
+    check(w.name, o, lse, O, LSE)
+    assert np.array_equal(bits(kc), kc_ref) and np.array_equal(bits(vc), vc_ref)

@@ -251,3 +251,73 @@ def random_paged(seed, lens, Hq, Hkv, d, page_size, pool_pages, split_tokens=512
             vc[last, tail:] = float("nan")
     return Paged(f"paged_s{seed}", q, kc, vc, table, lens, page_size, split_tokens,
                  1.0 / math.sqrt(d), window_left, {"spare_page": spare})
+
+
+@dataclass
+class KVCache:
+    """Chunked prefill over a paged cache: q (B, Lq, Hq, d); caches
+    [num_pages, page_size, Hkv, d]; cache_seqlens = keys already cached;
+    k_new / v_new (B, Lq, Hkv, d) or None."""
+    name: str
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    k_new: object
+    v_new: object
+    block_table: np.ndarray
+    cache_seqlens: np.ndarray
+    page_size: int
+    scale: float
+    causal: bool
+    window: tuple
+
+
+def random_kvcache(seed, lens, Lq, Hq, Hkv, d, page_size, append=True, causal=True,
+                   window=(-1, -1), spare_pages=3):
+    """Paged cache holding lens[b] tokens per request, plus (when appending)
+    pages already allocated for the Lq new tokens.  Draw order: page
+    permutation, q, K pool, V pool, k_new, v_new.  Unassigned pages and slots
+    at or past each request's final length are NaN, so a wrong read shows."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int32)
+    total = lens.astype(np.int64) + (Lq if append else 0)
+    npages = -(-total // page_size)
+    pool = int(npages.sum()) + spare_pages
+    max_blocks = int(max(1, npages.max()))
+    perm = rng.permutation(pool).astype(np.int32)
+    spare = int(perm[int(npages.sum())])
+    table = np.full((len(lens), max_blocks), spare, dtype=np.int32)
+    off = 0
+    for b in range(len(lens)):
+        table[b, :npages[b]] = perm[off:off + npages[b]]
+        off += int(npages[b])
+    q = bf16_normal(rng, (len(lens), Lq, Hq, d))
+    kc = bf16_normal(rng, (pool, page_size, Hkv, d))
+    vc = bf16_normal(rng, (pool, page_size, Hkv, d))
+    assigned = np.zeros(pool, dtype=bool)
+    assigned[perm[:int(npages.sum())]] = True
+    kc[torch.from_numpy(~assigned)] = float("nan")
+    vc[torch.from_numpy(~assigned)] = float("nan")
+    for b in range(len(lens)):
+        # slots from the cached length on are NaN until the append fills them
+        for pos in range(int(lens[b]), int(npages[b]) * page_size):
+            pg = int(table[b, pos // page_size])
+            kc[pg, pos % page_size] = float("nan")
+            vc[pg, pos % page_size] = float("nan")
+    kn = vn = None
+    if append:
+        kn = bf16_normal(rng, (len(lens), Lq, Hkv, d))
+        vn = bf16_normal(rng, (len(lens), Lq, Hkv, d))
+    return KVCache(f"kvcache_s{seed}", q, kc, vc, kn, vn, table, lens, page_size,
+                   1.0 / math.sqrt(d), causal, window)
+
+
+def chunked_prefill(seed=6):
+    """A chunk of 512 new tokens per request appended to, and attending over,
+    a paged cache of 2048..6144 cached tokens: 4 requests, Hq=32, Hkv=8,
+    d=128, 16-token pages, causal.  Cache lengths are drawn first."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(2048, 6144, 4, endpoint=True).astype(np.int32)
+    w = random_kvcache(seed + 1000, lens, 512, 32, 8, 128, 16, append=True)
+    w.name = "chunked_prefill_b4_lq512_h32_kv8_d128_p16"
+    return w
