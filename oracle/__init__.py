@@ -29,7 +29,8 @@ Readings where the pages are silent (each listed in the design doc):
   unbounded window side; query head h uses KV head h // (Hq // Hkv); LSE is the
   natural-log log-sum-exp of the scaled scores; a row with no visible key has
   O = 0 and LSE = -inf; new K/V rows are appended at positions
-  cache_seqlens[b] + i.
+  cache_seqlens[b] + i; softcap acts on the scaled logits and the ALiBi bias,
+  -slope * |i + Lk - Lq - j|, is added after it, both before the mask.
 
 Inputs are numpy arrays; a uint16 array is taken as bfloat16 bit patterns
 (numpy has no bfloat16 type) and converted exactly to float64.
@@ -42,6 +43,7 @@ closed forms, invariants, a pure-Python brute force and PyTorch's CPU
 from .attention import (
     key_visibility,
     attend_rows,
+    alibi_bias,
     attention_ref,
     attention_rows_ref,
     attention_varlen_ref,
@@ -57,6 +59,7 @@ from .attention import (
 __all__ = [
     "key_visibility",
     "attend_rows",
+    "alibi_bias",
     "attention_ref",
     "attention_rows_ref",
     "attention_varlen_ref",

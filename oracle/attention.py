@@ -45,16 +45,24 @@ def key_visibility(Lq, Lk, causal, window_left=-1, window_right=-1, rows=None):
     return vis
 
 
-def attend_rows(q_rows, k, v, scale, vis):
+def attend_rows(q_rows, k, v, scale, vis, softcap=0.0, bias=None):
     """Standard attention for a block of query rows of one head.
 
     "FlashAttention-3 vs naive attention", sec. 1.1: S = scale * Q K^T (+mask),
     P = softmax(S), O = P V.  Softmax is the usual max-subtracted form (same
     page, sec. 6.1).  Returns O (n, dv), LSE (n,) with LSE = m + ln l, and P
     (n, Lk).  Rows with no visible key give O = 0, LSE = -inf, P = 0.
+
+    Score modifiers ("flash-attention" skill page, sec. 3.3): softcap > 0
+    replaces each logit x = scale * q.k by softcap * tanh(x / softcap); bias
+    (n, Lk), e.g. ALiBi's, is then added.  Both come before the mask.
     """
     q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
     s = scale * (q_rows @ k.T)                      # S, materialised
+    if softcap > 0:
+        s = softcap * np.tanh(s / softcap)
+    if bias is not None:
+        s = s + bias
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1) if s.shape[1] > 0 else np.full(s.shape[0], -np.inf)
     m_safe = np.where(np.isfinite(m), m, 0.0)
@@ -69,6 +77,23 @@ def attend_rows(q_rows, k, v, scale, vis):
     return o, lse, p
 
 
+def alibi_bias(rows, Lq, Lk, slope):
+    """ALiBi bias for query rows ``rows`` against keys 0..Lk-1 ("flash-attention"
+    skill page, sec. 3.3: per-head alibi_slopes, used in place of RoPE).
+    Reading taken (the page gives no formula): -slope * |i + (Lk - Lq) - j|,
+    i.e. a penalty linear in the distance between the query's position
+    (bottom-right alignment, as for the causal mask) and the key."""
+    pos = np.asarray(rows, dtype=np.int64)[:, None] + (Lk - Lq)
+    j = np.arange(Lk, dtype=np.int64)[None, :]
+    return -float(slope) * np.abs(pos - j).astype(np.float64)
+
+
+def _slope(alibi_slopes, b, h):
+    """Slope of (batch b, query head h) from alibi_slopes of shape (Hq,) or (B, Hq)."""
+    a = np.asarray(alibi_slopes, dtype=np.float64)
+    return a[h] if a.ndim == 1 else a[b, h]
+
+
 def _kv_head(h, Hq, Hkv):
     """GQA/MQA broadcast ("flash-attention" skill page, appendix on GQA/MQA):
     Hkv divides Hq and query heads [g*G, (g+1)*G) share KV head g, G = Hq/Hkv
@@ -79,7 +104,7 @@ def _kv_head(h, Hq, Hkv):
 
 
 def attention_rows_ref(q, k, v, b, h, rows, softmax_scale=None, causal=False,
-                       window=(-1, -1), return_probs=False):
+                       window=(-1, -1), return_probs=False, softcap=0.0, alibi_slopes=None):
     """Selected query rows of one (batch b, query head h) of dense attention.
 
     q: (B, Lq, Hq, d); k, v: (B, Lk, Hkv, d).  Returns O (n, d), LSE (n,)
@@ -91,13 +116,14 @@ def attention_rows_ref(q, k, v, b, h, rows, softmax_scale=None, causal=False,
     g = _kv_head(h, Hq, Hkv)
     rows = np.asarray(rows, dtype=np.int64)
     vis = key_visibility(Lq, Lk, causal, window[0], window[1], rows=rows)
+    bias = None if alibi_slopes is None else alibi_bias(rows, Lq, Lk, _slope(alibi_slopes, b, h))
     o, lse, p = attend_rows(_f64(q[b, rows, h, :]), _f64(k[b, :, g, :]),
-                            _f64(v[b, :, g, :]), scale, vis)
+                            _f64(v[b, :, g, :]), scale, vis, softcap, bias)
     return (o, lse, p) if return_probs else (o, lse)
 
 
 def attention_ref(q, k, v, softmax_scale=None, causal=False, window=(-1, -1),
-                  row_block=1024):
+                  row_block=1024, softcap=0.0, alibi_slopes=None):
     """Dense attention over (B, L, H, d) tensors, the layout of the skill
     page's flash_attn_func (sec. 3.1/3.2); default scale 1/sqrt(headdim).
 
@@ -118,14 +144,17 @@ def attention_ref(q, k, v, softmax_scale=None, causal=False, window=(-1, -1),
             for r0 in range(0, Lq, row_block):
                 rows = np.arange(r0, min(Lq, r0 + row_block))
                 vis = key_visibility(Lq, Lk, causal, window[0], window[1], rows=rows)
-                o, lse, _ = attend_rows(q[b, rows, h, :], kk, vv, scale, vis)
+                bias = (None if alibi_slopes is None
+                        else alibi_bias(rows, Lq, Lk, _slope(alibi_slopes, b, h)))
+                o, lse, _ = attend_rows(q[b, rows, h, :], kk, vv, scale, vis, softcap, bias)
                 O[b, rows, h, :] = o
                 LSE[b, h, rows] = lse
     return O, LSE
 
 
 def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale=None,
-                         causal=False, window=(-1, -1), row_block=1024):
+                         causal=False, window=(-1, -1), row_block=1024, softcap=0.0,
+                         alibi_slopes=None):
     """Packed variable-length attention (skill page sec. 3.4 and the appendix on
     continuous batching): sequences are concatenated along the token axis,
     cu_seqlens holds batch+1 cumulative offsets, and no token attends across
@@ -144,8 +173,12 @@ def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale=None
         qs, qe, ks, ke = cq[b], cq[b + 1], ck[b], ck[b + 1]
         if qe == qs:
             continue
+        sl = None
+        if alibi_slopes is not None:
+            a = np.asarray(alibi_slopes, dtype=np.float64)
+            sl = a if a.ndim == 1 else a[b]
         o, lse = attention_ref(q[None, qs:qe], k[None, ks:ke], v[None, ks:ke],
-                               softmax_scale, causal, window, row_block)
+                               softmax_scale, causal, window, row_block, softcap, sl)
         O[qs:qe] = o[0]
         LSE[:, qs:qe] = lse[0]
     return O, LSE
@@ -214,7 +247,7 @@ def append_paged_ref(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens,
 
 def attention_kvcache_ref(q, k_cache, v_cache, block_table, cache_seqlens, page_size,
                           k_new=None, v_new=None, softmax_scale=None, causal=True,
-                          window=(-1, -1)):
+                          window=(-1, -1), softcap=0.0, alibi_slopes=None):
     """Attention of several new query tokens over a paged KV cache (chunked
     prefill; "flash-attention" skill page, sec. 3.5 and the appendix on
     PagedAttention).  When k_new / v_new are given they are first appended at
@@ -241,7 +274,12 @@ def attention_kvcache_ref(q, k_cache, v_cache, block_table, cache_seqlens, page_
         n = int(cache_seqlens[b]) + extra
         kk = _f64(gather_paged(k_cache, block_table[b], n, page_size))[None]
         vv = _f64(gather_paged(v_cache, block_table[b], n, page_size))[None]
-        o, lse = attention_ref(q[b:b + 1], kk, vv, softmax_scale, causal, window)
+        sl = None
+        if alibi_slopes is not None:
+            a = np.asarray(alibi_slopes, dtype=np.float64)
+            sl = a if a.ndim == 1 else a[b]
+        o, lse = attention_ref(q[b:b + 1], kk, vv, softmax_scale, causal, window,
+                               softcap=softcap, alibi_slopes=sl)
         O[b] = o[0]
         LSE[b] = lse[0]
     return O, LSE, k_cache, v_cache

@@ -522,6 +522,151 @@ def test_kvcache_planted_mistakes_are_caught(monkeypatch):
         monkeypatch.setattr(oracle_attention, "gather_paged", orig_gather)
 
 
+# ---------------------------------------------------- softcap and ALiBi slopes
+def test_softcap_large_cap_is_plain_attention():
+    q, k, v = rand(2, 9, 4, 8), rand(2, 11, 2, 8), rand(2, 11, 2, 8)
+    O, LSE = oracle.attention_ref(q, k, v, 0.4, True)
+    Oc, LSEc = oracle.attention_ref(q, k, v, 0.4, True, softcap=1e9)
+    assert np.abs(O - Oc).max() < 1e-9 and np.abs(LSE - LSEc).max() < 1e-9
+
+
+def test_softcap_saturation_gives_mean_and_cap_plus_log_count():
+    # every logit ~ +1e4: tanh saturates, each visible key scores exactly cap
+    d, L = 8, 12
+    u = np.ones(d) / math.sqrt(d)
+    k = (40.0 * u + 1e-3 * rand(L, d))[None, :, None, :]
+    q = (1e4 * u)[None, None, None, :].repeat(L, 1)
+    v = rand(1, L, 1, d)
+    O, LSE = oracle.attention_ref(q, k, v, 1.0, True, softcap=3.0)
+    for i in range(L):
+        assert np.abs(O[0, i, 0] - v[0, :i + 1, 0].mean(0)).max() < 1e-12
+        assert abs(LSE[0, 0, i] - (3.0 + math.log(i + 1))) < 1e-12
+
+
+def test_alibi_zero_slopes_is_plain_attention():
+    q, k, v = rand(2, 7, 4, 8), rand(2, 10, 2, 8), rand(2, 10, 2, 8)
+    O, LSE = oracle.attention_ref(q, k, v, 0.4, False, (3, 2))
+    Oa, LSEa = oracle.attention_ref(q, k, v, 0.4, False, (3, 2), alibi_slopes=np.zeros(4))
+    assert np.array_equal(O, Oa) and np.array_equal(LSE, LSEa)
+
+
+@pytest.mark.parametrize("slope", [0.05, 0.5, 2.0])
+def test_alibi_zero_q_closed_form(slope):
+    # Q = 0: logits are -slope * (pos_i - j) over the causal keys j <= pos_i, a
+    # geometric series: LSE = ln sum_{t=0}^{pos} e^{-slope t}; identity V exposes P
+    Lq, Lk = 5, 9
+    q = np.zeros((1, Lq, 2, Lk))
+    k = rand(1, Lk, 1, Lk)
+    v = np.eye(Lk)[None, :, None, :]
+    O, LSE = oracle.attention_ref(q, k, v, 0.7, True, alibi_slopes=np.array([slope, 2 * slope]))
+    for h, sl in enumerate([slope, 2 * slope]):
+        for i in range(Lq):
+            pos = i + Lk - Lq
+            z = (1 - math.exp(-sl * (pos + 1))) / (1 - math.exp(-sl))
+            assert abs(LSE[0, h, i] - math.log(z)) < 1e-12
+            want = np.array([math.exp(-sl * (pos - j)) / z if j <= pos else 0.0 for j in range(Lk)])
+            assert np.abs(O[0, i, h] - want).max() < 1e-13
+
+
+def brute_force_mod(q, k, v, scale, causal, wl, wr, softcap, slopes):
+    """brute_force with the score modifiers written out per score."""
+    B, Lq, Hq, d = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    O = np.zeros((B, Lq, Hq, d))
+    LSE = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            sl = slopes[h] if slopes.ndim == 1 else slopes[b, h]
+            for i in range(Lq):
+                p_i = i + Lk - Lq
+                keys = [j for j in range(Lk)
+                        if (not causal or j <= p_i) and (wl < 0 or j >= p_i - wl)
+                        and (wr < 0 or j <= p_i + wr)]
+                if not keys:
+                    LSE[b, h, i] = -math.inf
+                    continue
+                s = {}
+                for j in keys:
+                    x = scale * math.fsum(q[b, i, h, t] * k[b, j, g, t] for t in range(d))
+                    if softcap > 0:
+                        x = softcap * math.tanh(x / softcap)
+                    s[j] = x - sl * abs(p_i - j)
+                m = max(s.values())
+                e = {j: math.exp(s[j] - m) for j in keys}
+                l = math.fsum(e.values())
+                for t in range(d):
+                    O[b, i, h, t] = math.fsum(e[j] * v[b, j, g, t] for j in keys) / l
+                LSE[b, h, i] = m + math.log(l)
+    return O, LSE
+
+
+@pytest.mark.parametrize("softcap", [0.0, 0.8])
+@pytest.mark.parametrize("per_batch", [False, True])
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (False, (2, 1))])
+def test_brute_force_softcap_alibi(softcap, per_batch, causal, window):
+    rng = np.random.default_rng(31)
+    q, k, v = rand(2, 5, 4, 3), rand(2, 8, 2, 3), rand(2, 8, 2, 3)
+    slopes = rng.uniform(0.0, 0.6, (2, 4) if per_batch else 4)
+    O, LSE = oracle.attention_ref(q, k, v, 0.9, causal, window, softcap=softcap, alibi_slopes=slopes)
+    Ob, LSEb = brute_force_mod(q, k, v, 0.9, causal, *window, softcap, slopes)
+    assert np.abs(O - Ob).max() < 1e-12 and np.abs(LSE - LSEb).max() < 1e-12
+
+
+def test_modifiers_varlen_and_kvcache_match_dense():
+    rng = np.random.default_rng(32)
+    lens = [4, 9, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v = rand(cu[-1], 4, 3), rand(cu[-1], 2, 3), rand(cu[-1], 2, 3)
+    slopes = rng.uniform(0.1, 0.5, (3, 4))
+    O, LSE = oracle.attention_varlen_ref(q, k, v, cu, cu, 0.8, True, softcap=1.5, alibi_slopes=slopes)
+    for b in range(3):
+        s, e = cu[b], cu[b + 1]
+        Ob, LSEb = brute_force_mod(q[None, s:e], k[None, s:e], v[None, s:e], 0.8, True, -1, -1,
+                                   1.5, slopes[b])
+        assert np.abs(O[s:e] - Ob[0]).max() < 1e-12 and np.abs(LSE[:, s:e] - LSEb[0]).max() < 1e-12
+    qc, kc, vc, table, lens2, ps, kn, vn = _kvcache_case(33)
+    Okv, LSEkv, kc2, vc2 = oracle.attention_kvcache_ref(qc, kc, vc, table, lens2, ps, kn, vn, 0.6, True,
+                                                        softcap=2.0, alibi_slopes=slopes[:2])
+    for b in range(2):
+        n = lens2[b] + qc.shape[1]
+        kk = oracle.gather_paged(kc2, table[b], n, ps)[None]
+        vv = oracle.gather_paged(vc2, table[b], n, ps)[None]
+        Ob, LSEb = brute_force_mod(qc[b:b + 1], kk, vv, 0.6, True, -1, -1, 2.0, slopes[b])
+        assert np.abs(Okv[b] - Ob[0]).max() < 1e-12 and np.abs(LSEkv[b] - LSEb[0]).max() < 1e-12
+
+
+def test_modifier_planted_mistakes_are_caught(monkeypatch):
+    orig_bias, orig_attend = oracle_attention.alibi_bias, oracle_attention.attend_rows
+
+    def bias_wrong_sign(rows, Lq, Lk, slope):
+        return -orig_bias(rows, Lq, Lk, slope)
+
+    def bias_top_left(rows, Lq, Lk, slope):
+        return orig_bias(rows, Lk, Lk, slope)
+
+    def cap_before_scale(q_rows, k, v, scale, vis, softcap=0.0, bias=None):
+        if softcap <= 0:
+            return orig_attend(q_rows, k, v, scale, vis, softcap, bias)
+        s = softcap * np.tanh((np.asarray(q_rows, float) @ np.asarray(k, float).T) / softcap)
+        qq = np.asarray(q_rows, float) * 0   # recompute: scale applied after the cap
+        o, lse, p = orig_attend(qq, k, v, 1.0, vis, 0.0, scale * s + (0 if bias is None else bias))
+        return o, lse, p
+
+    checks = [
+        ("alibi_bias", bias_wrong_sign, lambda: test_alibi_zero_q_closed_form(0.5)),
+        ("alibi_bias", bias_top_left, lambda: test_alibi_zero_q_closed_form(0.5)),
+        ("attend_rows", cap_before_scale, lambda: test_brute_force_softcap_alibi(0.8, False, True, (-1, -1))),
+    ]
+    for name, mut, pin in checks:
+        monkeypatch.setattr(oracle_attention, name, mut)
+        with pytest.raises(AssertionError):
+            pin()
+        monkeypatch.setattr(oracle_attention, "alibi_bias", orig_bias)
+        monkeypatch.setattr(oracle_attention, "attend_rows", orig_attend)
+
+
 # ---------------------------------------------------------- planted mistakes
 def _pin_suite(attn):
     """A few pins rerun against a (possibly mutated) attention function; returns
@@ -558,14 +703,14 @@ def test_planted_mistakes_are_caught(monkeypatch):
     def off_by_one(Lq, Lk, causal, wl=-1, wr=-1, rows=None):
         return orig_vis(Lq, Lk, causal, wl + 1 if wl >= 0 else wl, wr, rows=rows)
 
-    def no_scale(q_rows, k, v, scale, vis):
-        return orig_attend(q_rows, k, v, 1.0, vis)
+    def no_scale(q_rows, k, v, scale, vis, softcap=0.0, bias=None):
+        return orig_attend(q_rows, k, v, 1.0, vis, softcap, bias)
 
     def modulo_heads(h, Hq, Hkv):
         return h % Hkv
 
-    def v_transposed(q_rows, k, v, scale, vis):
-        o, lse, p = orig_attend(q_rows, k, v, scale, vis)
+    def v_transposed(q_rows, k, v, scale, vis, softcap=0.0, bias=None):
+        o, lse, p = orig_attend(q_rows, k, v, scale, vis, softcap, bias)
         return (p @ np.asarray(v)[::-1], lse, p)                  # wrong V rows
 
     for name, mut in [("key_visibility", top_left), ("key_visibility", off_by_one),
