@@ -27,22 +27,25 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 
 _lib = None
 
+# softcap, alibi_slopes, alibi_batch_stride (prefill entry points)
+_MODS = [ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
+
 _EXPORTS = {
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_fwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p]
-               + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                       ctypes.c_void_p]),
+               + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+               + _MODS + [ctypes.c_void_p]),
     "fa_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 2
                       + [ctypes.c_int] * 8 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
-                                              ctypes.c_int, ctypes.c_void_p]),
+                                              ctypes.c_int] + _MODS + [ctypes.c_void_p]),
     "fa_decode_paged_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 6),
     "fa_decode_paged": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 2
                         + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                                 ctypes.c_void_p, ctypes.c_size_t,
                                                 ctypes.c_void_p]),
     "fa_fwd_kvcache": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 8
-                       + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                          ctypes.c_void_p]),
+                       + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                       + _MODS + [ctypes.c_void_p]),
 }
 
 
@@ -128,9 +131,25 @@ def lengths_from_cu_seqlens(cu):
     return np.diff(cu).astype(np.int32)
 
 
+def _mods(softcap, alibi_slopes, B, Hq):
+    """(softcap, slopes pointer, batch stride) for the C call; slopes is a float32
+    device tensor of shape (Hq,) or (B, Hq), or None."""
+    if alibi_slopes is None:
+        return float(softcap), None, 0
+    torch = _torch()
+    _need(alibi_slopes, "alibi_slopes", torch.float32)
+    if tuple(alibi_slopes.shape) == (Hq,):
+        return float(softcap), _ptr(alibi_slopes), 0
+    if tuple(alibi_slopes.shape) == (B, Hq):
+        return float(softcap), _ptr(alibi_slopes), Hq
+    raise ValueError("alibi_slopes must be (Hq,) or (B, Hq)")
+
+
 def fa_fwd(q, k, v, softmax_scale=None, causal=False, window=(-1, -1), out=None,
-           lse=None, return_lse=True, stream=None):
-    """Dense prefill: q (B, Lq, Hq, d), k/v (B, Lk, Hkv, d) bf16 -> O, LSE (B, Hq, Lq)."""
+           lse=None, return_lse=True, stream=None, softcap=0.0, alibi_slopes=None):
+    """Dense prefill: q (B, Lq, Hq, d), k/v (B, Lk, Hkv, d) bf16 -> O, LSE (B, Hq, Lq).
+    softcap > 0 caps the logits (c*tanh(x/c)); alibi_slopes (Hq,) or (B, Hq)
+    float32 adds -slope*|i + Lk - Lq - j|."""
     torch = _torch()
     lib = load_library()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -148,14 +167,15 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, window=(-1, -1), out=None,
     if lse is not None:
         _need(lse, "lse", torch.float32, 3)
     st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Lq, Lk, Hq, Hkv, d,
-                    scale, int(bool(causal)), int(window[0]), int(window[1]), _stream(stream))
+                    scale, int(bool(causal)), int(window[0]), int(window[1]),
+                    *_mods(softcap, alibi_slopes, B, Hq), _stream(stream))
     _check("fa_fwd", st)
     return out, lse
 
 
 def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                   softmax_scale=None, causal=False, window=(-1, -1), out=None, lse=None,
-                  return_lse=True, stream=None):
+                  return_lse=True, stream=None, softcap=0.0, alibi_slopes=None):
     """Packed varlen prefill: q (total_q, Hq, d), k/v (total_k, Hkv, d), cu_seqlens int32
     device tensors of length B+1 -> O, LSE (Hq, total_q)."""
     torch = _torch()
@@ -179,7 +199,8 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
     st = lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
                            _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k), total_q,
                            total_k, Hq, Hkv, d, scale, int(bool(causal)), int(window[0]),
-                           int(window[1]), _stream(stream))
+                           int(window[1]), *_mods(softcap, alibi_slopes, B, Hq),
+                           _stream(stream))
     _check("fa_fwd_varlen", st)
     return out, lse
 
@@ -229,7 +250,7 @@ def fa_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, softmax_sca
 
 def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=None,
                    softmax_scale=None, causal=True, window=(-1, -1), out=None, lse=None,
-                   return_lse=True, stream=None):
+                   return_lse=True, stream=None, softcap=0.0, alibi_slopes=None):
     """Chunked prefill over a paged KV cache: q (B, Lq, Hq, d) attends to each
     request's cache_seqlens[b] cached keys, after k_new / v_new (B, Lq, Hkv, d),
     if given, are written into the caches at positions cache_seqlens[b] + i
@@ -265,7 +286,8 @@ def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, 
     st = lib.fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
                             _ptr(block_table), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
                             B, Lq, Hq, Hkv, d, num_pages, page_size, block_table.shape[1],
-                            scale, int(bool(causal)), int(wl), int(wr), _stream(stream))
+                            scale, int(bool(causal)), int(wl), int(wr),
+                            *_mods(softcap, alibi_slopes, B, Hq), _stream(stream))
     _check("fa_fwd_kvcache", st)
     return out, lse
 

@@ -34,6 +34,22 @@ fa_status check_tensors(const void* q, const void* k, const void* v, const void*
   return FA_OK;
 }
 
+// softcap >= 0 (0: off); ALiBi slopes NULL or float32 with batch stride 0 (one
+// slope per query head) or Hq (one per batch and head).
+fa_status check_mods(float softcap, const float* alibi, int alibi_bstride, int Hq) {
+  if (!(softcap >= 0.f) || !isfinite(softcap)) return FA_ERR_INVALID_ARG;
+  if (alibi && (!aligned(alibi, 4) || (alibi_bstride != 0 && alibi_bstride != Hq))) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+void set_mods(fa::PrefillParams& p, float scale, float softcap, const float* alibi, int alibi_bstride) {
+  p.cap_in = softcap > 0.f ? scale / softcap : 0.f;
+  p.cap_out = softcap > 0.f ? softcap / scale : 0.f;
+  p.alibi = alibi;
+  p.alibi_bstride = alibi ? alibi_bstride : 0;
+  p.alibi_scale = 1.f / scale;
+}
+
 // XCD-aware mapping needs the KV-group count to split evenly over 8 XCDs.
 int xcd_groups(int kv_groups) { return (kv_groups > 0 && kv_groups % 8 == 0) ? kv_groups : 0; }
 
@@ -63,10 +79,12 @@ const char* fa_status_string(fa_status status) {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Lq, int Lk, int Hq, int Hkv, int d,
                  float softmax_scale, int causal, int window_left, int window_right,
+                 float softcap, const float* alibi_slopes, int alibi_batch_stride,
                  void* stream) {
   fa_status st = check_common(Hq, Hkv, d, softmax_scale, causal, window_left, window_right);
   if (st != FA_OK) return st;
   if ((st = check_tensors(q, k, v, o, lse)) != FA_OK) return st;
+  if ((st = check_mods(softcap, alibi_slopes, alibi_batch_stride, Hq)) != FA_OK) return st;
   if (B < 1 || Lq < 1 || Lk < 1) return FA_ERR_INVALID_ARG;
   // per-batch tensors are addressed with 32-bit byte offsets
   if ((int64_t)Lq * Hq * d >= kMaxBatchElems || (int64_t)Lk * Hkv * d >= kMaxBatchElems)
@@ -87,6 +105,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.lse_seq_stride = Lq;
   p.scale_log2 = softmax_scale * kLog2e;
   p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  set_mods(p, softmax_scale, softcap, alibi_slopes, alibi_batch_stride);
   p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
   p.xcd_groups = xcd_groups(B * Hkv);
   // KV groups per XCD chunk: about one XCD's worth of resident workgroups
@@ -100,10 +119,12 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
                         int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
                         int Hq, int Hkv, int d, float softmax_scale, int causal,
-                        int window_left, int window_right, void* stream) {
+                        int window_left, int window_right, float softcap,
+                        const float* alibi_slopes, int alibi_batch_stride, void* stream) {
   fa_status st = check_common(Hq, Hkv, d, softmax_scale, causal, window_left, window_right);
   if (st != FA_OK) return st;
   if ((st = check_tensors(q, k, v, o, lse)) != FA_OK) return st;
+  if ((st = check_mods(softcap, alibi_slopes, alibi_batch_stride, Hq)) != FA_OK) return st;
   if (!cu_seqlens_q || !cu_seqlens_k || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
     return FA_ERR_INVALID_ARG;
   if (B < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
@@ -129,6 +150,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   p.lse_seq_stride = total_q;
   p.scale_log2 = softmax_scale * kLog2e;
   p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  set_mods(p, softmax_scale, softcap, alibi_slopes, alibi_batch_stride);
   // tile slots: sequence b owns [cu_q[b]/128 + b, cu_q[b+1]/128 + b + 1)
   p.num_q_tiles = total_q / fa::kBlockM + B;
   p.xcd_groups = xcd_groups(Hkv);
@@ -143,10 +165,12 @@ fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
                          void* o, float* lse, int B, int Lq, int Hq, int Hkv, int d,
                          int num_pages, int page_size, int max_blocks_per_seq,
                          float softmax_scale, int causal, int window_left, int window_right,
+                         float softcap, const float* alibi_slopes, int alibi_batch_stride,
                          void* stream) {
   fa_status st = check_common(Hq, Hkv, d, softmax_scale, causal, window_left, window_right);
   if (st != FA_OK) return st;
   if ((st = check_tensors(q, k_cache, v_cache, o, lse)) != FA_OK) return st;
+  if ((st = check_mods(softcap, alibi_slopes, alibi_batch_stride, Hq)) != FA_OK) return st;
   if ((k_new == nullptr) != (v_new == nullptr)) return FA_ERR_INVALID_ARG;
   if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) return FA_ERR_INVALID_ARG;
   if (!block_table || !cache_seqlens || !aligned(block_table, 4) || !aligned(cache_seqlens, 4))
@@ -191,6 +215,7 @@ fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
   p.lse_seq_stride = Lq;
   p.scale_log2 = softmax_scale * kLog2e;
   p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  set_mods(p, softmax_scale, softcap, alibi_slopes, alibi_batch_stride);
   p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
   p.xcd_groups = xcd_groups(B * Hkv);
   p.chunk_groups = (int)std::max<int64_t>(1, fa::kPrefillSlotsPerXcd / ((int64_t)p.group * p.num_q_tiles));

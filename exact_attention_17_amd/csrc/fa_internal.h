@@ -46,6 +46,11 @@ struct PrefillParams {
   const int* cache_seqlens;
   int page_size, max_blocks, append_len;
   int page_shift;          // log2(page_size) when a power of two, else -1
+  // score modifiers, in units of the raw dot product q.k (logit = scale * q.k)
+  float cap_in, cap_out;   // softcap c: q.k -> cap_out * tanh(cap_in * q.k); cap_in = 0: off
+  const float* alibi;      // slopes, NULL: off; slope of (b, h) = alibi[b * alibi_bstride + h]
+  int alibi_bstride;
+  float alibi_scale;       // 1 / softmax_scale
 };
 
 // Copy new tokens' K/V rows into a paged cache (see fa_fwd_kvcache).

@@ -159,7 +159,9 @@ __device__ __forceinline__ WorkItem map_work_varlen(const PrefillParams& p, int 
 
 // MODE 0: dense (B, L, H, d); 1: packed varlen; 2: queries dense (B, Lq, Hq, d),
 // keys from a paged KV cache.
-template <int D, int MODE>
+// MODS: softcap and/or ALiBi requested (a separate instance, so the plain
+// kernel carries none of their registers).
+template <int D, int MODE, bool MODS>
 __global__ __launch_bounds__(kPrefillThreads, 2)
 void prefill_fwd_kernel(PrefillParams p) {
   constexpr bool VARLEN = MODE == 1, PAGED = MODE == 2;
@@ -334,6 +336,27 @@ void prefill_fwd_kernel(PrefillParams p) {
       for (int t = 0; t < KSTEPS; ++t) S[kh] = mfma32x32x16(k_frag(buf, kh, t), qf[t], S[kh]);
     }
   };
+  // Score modifiers (skill page sec. 3.3), on the raw dot products before the
+  // mask: softcap replaces the logit x = scale*s by c*tanh(x/c), i.e. s by
+  // (c/scale)*tanh((scale/c)*s), with tanh(y) = 1 - 2/(e^{2y} + 1); the ALiBi
+  // bias -slope*|pos - key| of the logit is -(slope/scale)*|pos - key| on s.
+  const float alibi_s = MODS && p.alibi ? p.alibi[(int64_t)w.b * p.alibi_bstride + w.h] * p.alibi_scale : 0.f;
+  auto modify = [&](f32x16 (&S)[2], int kb) {
+    if (!MODS) return;
+    const float two_log2e = 2.f * 1.4426950408889634f * p.cap_in;
+    const int pos = row + delta;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = S[kh][r];
+        if (p.cap_in > 0.f)
+          x = p.cap_out * (1.f - 2.f * __builtin_amdgcn_rcpf(exp2_fast(x * two_log2e) + 1.f));
+        const int key = kb + 32 * kh + 8 * (r >> 2) + 4 * hi + (r & 3);
+        x -= alibi_s * (float)abs(pos - key);
+        S[kh][r] = x;
+      }
+  };
   // mask only on tiles that cut through some row's visible band
   auto mask_tile = [&](f32x16 (&S)[2], int kb) {
     if (kb >= wlo_last && kb + kBlockN <= whi_first) return;
@@ -475,6 +498,7 @@ void prefill_fwd_kernel(PrefillParams p) {
                   u32x4 (&Pprev)[4], u32x4 (&Pcur)[4]) {
     constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
     const int kb = kb0 + j * kBlockN;
+    modify(Scur, kb);
     mask_tile(Scur, kb);
     update_max(Scur, [&] {
       pv(nxt, Pprev);
@@ -525,7 +549,12 @@ hipError_t launch_prefill(const PrefillParams& p, int d, int mode, hipStream_t s
                                     : (int64_t)p.num_q_tiles * p.B * p.Hq;
   if (nblocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)nblocks), block(kPrefillThreads);
-#define FA_PREFILL(DD, MM) hipLaunchKernelGGL((prefill_fwd_kernel<DD, MM>), grid, block, 0, stream, p)
+  const bool mods = p.cap_in > 0.f || p.alibi != nullptr;
+#define FA_PREFILL(DD, MM)                                                                  \
+  do {                                                                                      \
+    if (mods) hipLaunchKernelGGL((prefill_fwd_kernel<DD, MM, true>), grid, block, 0, stream, p); \
+    else hipLaunchKernelGGL((prefill_fwd_kernel<DD, MM, false>), grid, block, 0, stream, p);     \
+  } while (0)
   if (d == 128) {
     if (mode == 0) FA_PREFILL(128, 0); else if (mode == 1) FA_PREFILL(128, 1); else FA_PREFILL(128, 2);
   } else {

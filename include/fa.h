@@ -33,6 +33,15 @@
  *     the keys to [i + Lk - Lq - left, i + Lk - Lq + right] inclusive;
  *     -1 leaves that side unbounded.  A row with no visible key gets O = 0
  *     and LSE = -inf.
+ *   - Score modifiers of the prefill entry points (fa_fwd, fa_fwd_varlen,
+ *     fa_fwd_kvcache; skill page sec. 3.3): softcap > 0 replaces each logit
+ *     x = softmax_scale * q.k by softcap * tanh(x / softcap) (0 = off; must
+ *     be finite and >= 0).  alibi_slopes (device float32, or NULL = off) adds
+ *     -slope * |i + Lk - Lq - j| to the logit of query row i and key j, after
+ *     the softcap and before the mask; the slope of (batch b, query head h)
+ *     is alibi_slopes[b * alibi_batch_stride + h], with alibi_batch_stride 0
+ *     (slopes of shape (Hq,)) or Hq (shape (B, Hq); for varlen, b is the
+ *     sequence index).  Paged decode takes neither.
  *   - Errors: every argument is validated on the host before any HIP call.
  *     On a non-zero status nothing has been enqueued and no output has been
  *     touched.  FA_ERR_HIP reports a failed kernel launch.  Device-side
@@ -72,6 +81,7 @@ const char* fa_status_string(fa_status status);
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Lq, int Lk, int Hq, int Hkv, int d,
                  float softmax_scale, int causal, int window_left, int window_right,
+                 float softcap, const float* alibi_slopes, int alibi_batch_stride,
                  void* stream);
 
 /*
@@ -91,7 +101,8 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
                         int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
                         int Hq, int Hkv, int d, float softmax_scale, int causal,
-                        int window_left, int window_right, void* stream);
+                        int window_left, int window_right, float softcap,
+                        const float* alibi_slopes, int alibi_batch_stride, void* stream);
 
 /*
  * Bytes of device workspace fa_decode_paged needs for these sizes (split
@@ -163,6 +174,7 @@ fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
                          void* o, float* lse, int B, int Lq, int Hq, int Hkv, int d,
                          int num_pages, int page_size, int max_blocks_per_seq,
                          float softmax_scale, int causal, int window_left, int window_right,
+                         float softcap, const float* alibi_slopes, int alibi_batch_stride,
                          void* stream);
 
 #ifdef __cplusplus

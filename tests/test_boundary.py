@@ -48,10 +48,11 @@ def test_status_strings(lib):
 
 def fwd(lib, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Lq=128, Lk=128, Hq=2, Hkv=1, d=64,
-             scale=0.125, causal=0, wl=-1, wr=-1)
+             scale=0.125, causal=0, wl=-1, wr=-1, cap=0.0, al=None, ab=0)
     a.update(kw)
     return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Lq"], a["Lk"], a["Hq"],
-                      a["Hkv"], a["d"], a["scale"], a["causal"], a["wl"], a["wr"], None)
+                      a["Hkv"], a["d"], a["scale"], a["causal"], a["wl"], a["wr"], a["cap"], a["al"],
+                      a["ab"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -62,6 +63,8 @@ def fwd(lib, **kw):
     (dict(scale=-1.0), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(causal=2), INVALID), (dict(wl=-2), INVALID), (dict(wr=-5), INVALID),
     (dict(Lq=1 << 20, Hq=64, d=128), INVALID),
+    (dict(cap=-1.0), INVALID), (dict(cap=float("nan")), INVALID), (dict(cap=float("inf")), INVALID),
+    (dict(al=P + 2), INVALID), (dict(al=P, ab=1), INVALID), (dict(al=P, ab=-2), INVALID),
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
@@ -69,17 +72,18 @@ def test_fwd_rejects(lib, kw, code):
 
 def varlen(lib, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, cq=P, ck=P, B=2, mq=10, mk=10, tq=16, tk=16, Hq=4, Hkv=2,
-             d=128, scale=0.1, causal=1, wl=-1, wr=-1)
+             d=128, scale=0.1, causal=1, wl=-1, wr=-1, cap=0.0, al=None, ab=0)
     a.update(kw)
     return lib.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"], a["mq"],
                              a["mk"], a["tq"], a["tk"], a["Hq"], a["Hkv"], a["d"], a["scale"],
-                             a["causal"], a["wl"], a["wr"], None)
+                             a["causal"], a["wl"], a["wr"], a["cap"], a["al"], a["ab"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(cq=None), INVALID), (dict(ck=P + 2), INVALID), (dict(B=0), INVALID),
     (dict(tq=-1), INVALID), (dict(mq=20), INVALID), (dict(mq=0), INVALID), (dict(mk=-1), INVALID),
-    (dict(d=80), UNSUPPORTED), (dict(Hq=5), INVALID),
+    (dict(d=80), UNSUPPORTED), (dict(Hq=5), INVALID), (dict(cap=-0.5), INVALID),
+    (dict(al=P, ab=3), INVALID),
 ])
 def test_varlen_rejects(lib, kw, code):
     assert varlen(lib, **kw) == code
@@ -126,11 +130,12 @@ def test_decode_rejects(lib, kw, code):
 
 def kvcache(lib, **kw):
     a = dict(q=P, kc=P, vc=P, kn=P, vn=P, bt=P, sl=P, o=P, lse=P, B=2, Lq=64, Hq=8, Hkv=2, d=128,
-             pages=64, ps=16, mb=8, scale=0.1, causal=1, wl=-1, wr=-1)
+             pages=64, ps=16, mb=8, scale=0.1, causal=1, wl=-1, wr=-1, cap=0.0, al=None, ab=0)
     a.update(kw)
     return lib.fa_fwd_kvcache(a["q"], a["kc"], a["vc"], a["kn"], a["vn"], a["bt"], a["sl"], a["o"],
                               a["lse"], a["B"], a["Lq"], a["Hq"], a["Hkv"], a["d"], a["pages"], a["ps"],
-                              a["mb"], a["scale"], a["causal"], a["wl"], a["wr"], None)
+                              a["mb"], a["scale"], a["causal"], a["wl"], a["wr"], a["cap"], a["al"],
+                              a["ab"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -141,6 +146,7 @@ def kvcache(lib, **kw):
     (dict(ps=8), UNSUPPORTED), (dict(ps=24), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
     (dict(Hkv=3), INVALID), (dict(scale=float("nan")), INVALID), (dict(causal=5), INVALID),
     (dict(wl=-3), INVALID), (dict(ps=1 << 16, Hkv=64), INVALID), (dict(mb=1 << 26, ps=16), INVALID),
+    (dict(cap=-2.0), INVALID), (dict(al=P + 1), INVALID),
 ])
 def test_kvcache_rejects(lib, kw, code):
     assert kvcache(lib, **kw) == code

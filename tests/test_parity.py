@@ -264,3 +264,62 @@ def test_full_chunked_prefill(fa):
     O, LSE, kc_ref, vc_ref = kvcache_ref(w)
     check(w.name, o, lse, O, LSE)
     assert np.array_equal(bits(kc), kc_ref) and np.array_equal(bits(vc), vc_ref)
+
+
+# ------------------------------------------------- softcap and ALiBi modifiers
+def alibi_slopes(Hq, B=None):
+    """The usual geometric ALiBi slopes 2^(-8 (h + 1) / Hq); per batch, scaled
+    by (b + 1) / B so each request differs."""
+    base = np.array([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)])
+    if B is None:
+        return base.astype(np.float32)
+    return np.stack([base * (b + 1) / B for b in range(B)]).astype(np.float32)
+
+
+# B, Lq, Lk, Hq, Hkv, d, causal, window, softcap, alibi ("none" | "head" | "batch")
+MOD_CASES = [
+    (2, 300, 300, 4, 2, 128, True, (-1, -1), 30.0, "none"),
+    (2, 300, 300, 4, 2, 128, True, (-1, -1), 0.0, "head"),
+    (2, 257, 257, 8, 2, 128, True, (64, 0), 5.0, "batch"),
+    (1, 129, 385, 4, 1, 64, True, (-1, -1), 2.0, "head"),
+    (1, 200, 200, 2, 2, 64, False, (-1, -1), 0.5, "batch"),
+]
+
+
+@pytest.mark.parametrize("case", MOD_CASES, ids=lambda c: f"L{c[1]}x{c[2]}-h{c[3]}-d{c[5]}-c{int(c[6])}-cap{c[8]}-{c[9]}")
+def test_dense_score_modifiers(fa, case):
+    B, Lq, Lk, Hq, Hkv, d, causal, window, cap, al = case
+    w = workloads.random_dense(700 + Lq + Lk + Hq, B, Lq, Lk, Hq, Hkv, d, causal, window)
+    slopes = None if al == "none" else alibi_slopes(Hq, B if al == "batch" else None)
+    o, lse = fa.fa_fwd(dev(w.q), dev(w.k), dev(w.v), w.scale, causal, window, softcap=cap,
+                       alibi_slopes=None if slopes is None else dev(torch.from_numpy(slopes)))
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_ref(bits(w.q), bits(w.k), bits(w.v), w.scale, causal, window,
+                                  softcap=cap, alibi_slopes=slopes)
+    check(f"mods{case}", o, lse, O, LSE)
+
+
+def test_varlen_and_kvcache_score_modifiers(fa):
+    w = workloads.random_varlen(731, [70, 300, 5, 160], 8, 2, 128, True, (-1, -1))
+    slopes = alibi_slopes(8, 4)
+    cu = dev(torch.from_numpy(w.cu_seqlens))
+    o, lse = fa.fa_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), cu, cu, w.max_seqlen, w.max_seqlen,
+                              w.scale, True, (-1, -1), softcap=8.0,
+                              alibi_slopes=dev(torch.from_numpy(slopes)))
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_varlen_ref(bits(w.q), bits(w.k), bits(w.v), w.cu_seqlens, w.cu_seqlens,
+                                         w.scale, True, (-1, -1), softcap=8.0, alibi_slopes=slopes)
+    check("varlen mods", o, lse, O, LSE)
+
+    kv = workloads.random_kvcache(732, [300, 17], 70, 8, 2, 128, 16, True, True)
+    sl = alibi_slopes(8)
+    kc, vc = dev(kv.k_cache), dev(kv.v_cache)
+    o, lse = fa.fa_fwd_kvcache(dev(kv.q), kc, vc, dev(torch.from_numpy(kv.block_table)),
+                               dev(torch.from_numpy(kv.cache_seqlens)), dev(kv.k_new), dev(kv.v_new),
+                               kv.scale, True, softcap=20.0, alibi_slopes=dev(torch.from_numpy(sl)))
+    torch.cuda.synchronize()
+    O, LSE, _, _ = oracle.attention_kvcache_ref(bits(kv.q), bits(kv.k_cache), bits(kv.v_cache),
+                                                kv.block_table, kv.cache_seqlens, kv.page_size,
+                                                bits(kv.k_new), bits(kv.v_new), kv.scale, True,
+                                                softcap=20.0, alibi_slopes=sl)
+    check("kvcache mods", o, lse, O, LSE)
