@@ -38,7 +38,18 @@ _EXPORTS = {
     "fa_fwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 2
                       + [ctypes.c_int] * 8 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int] + _MODS + [ctypes.c_void_p]),
+    "fa_varlen_plan": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4
+                       + [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
+    "fa_fwd_varlen_run": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 3
+                          + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int] + _MODS + [ctypes.c_void_p]),
     "fa_decode_paged_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 6),
+    "fa_decode_plan": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_int] * 5
+                       + [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
+    "fa_decode_paged_run": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int]
+                            + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 7
+                            + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fa_decode_paged": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 2
                         + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                                 ctypes.c_void_p, ctypes.c_size_t,
@@ -173,13 +184,8 @@ def fa_fwd(q, k, v, softmax_scale=None, causal=False, window=(-1, -1), out=None,
     return out, lse
 
 
-def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                  softmax_scale=None, causal=False, window=(-1, -1), out=None, lse=None,
-                  return_lse=True, stream=None, softcap=0.0, alibi_slopes=None):
-    """Packed varlen prefill: q (total_q, Hq, d), k/v (total_k, Hkv, d), cu_seqlens int32
-    device tensors of length B+1 -> O, LSE (Hq, total_q)."""
+def _varlen_args(q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse, return_lse):
     torch = _torch()
-    lib = load_library()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16, 3)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
@@ -196,6 +202,17 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    return out, lse, B, total_q, total_k, Hq, Hkv, d, scale
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                  softmax_scale=None, causal=False, window=(-1, -1), out=None, lse=None,
+                  return_lse=True, stream=None, softcap=0.0, alibi_slopes=None):
+    """Packed varlen prefill: q (total_q, Hq, d), k/v (total_k, Hkv, d), cu_seqlens int32
+    device tensors of length B+1 -> O, LSE (Hq, total_q)."""
+    lib = load_library()
+    out, lse, B, total_q, total_k, Hq, Hkv, d, scale = _varlen_args(
+        q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse, return_lse)
     st = lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
                            _ptr(cu_seqlens_k), B, int(max_seqlen_q), int(max_seqlen_k), total_q,
                            total_k, Hq, Hkv, d, scale, int(bool(causal)), int(window[0]),
@@ -205,18 +222,57 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_
     return out, lse
 
 
+def fa_varlen_plan(cu_seqlens_q, cu_seqlens_k, causal=False, window=(-1, -1)):
+    """Host plan for fa_fwd_varlen_run from HOST cumulative lengths (lists, numpy arrays or
+    CPU tensors of B+1 ints) -> numpy int32 array (num_items, 2) of (sequence, query tile),
+    heaviest first.  No GPU is needed."""
+    import numpy as np
+    lib = load_library()
+    cq = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64)).astype(np.int32)
+    ck = np.ascontiguousarray(np.asarray(cu_seqlens_k, dtype=np.int64)).astype(np.int32)
+    if cq.ndim != 1 or ck.shape != cq.shape or cq.size < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D of the same length >= 2")
+    B = cq.size - 1
+    n = ctypes.c_int(0)
+    args = (cq.ctypes.data_as(ctypes.c_void_p), ck.ctypes.data_as(ctypes.c_void_p), B,
+            int(bool(causal)), int(window[0]), int(window[1]))
+    _check("fa_varlen_plan", lib.fa_varlen_plan(*args, None, 0, ctypes.byref(n)))
+    plan = np.zeros((max(n.value, 1), 2), dtype=np.int32)
+    _check("fa_varlen_plan", lib.fa_varlen_plan(*args, plan.ctypes.data_as(ctypes.c_void_p),
+                                                 n.value, ctypes.byref(n)))
+    return plan[:n.value]
+
+
+def fa_fwd_varlen_run(q, k, v, cu_seqlens_q, cu_seqlens_k, plan, max_seqlen_q, max_seqlen_k,
+                      softmax_scale=None, causal=False, window=(-1, -1), out=None, lse=None,
+                      return_lse=True, stream=None, softcap=0.0, alibi_slopes=None):
+    """fa_fwd_varlen in the order of a plan from fa_varlen_plan (same lengths, causal flag and
+    window), uploaded as a device int32 tensor (num_items, 2)."""
+    torch = _torch()
+    lib = load_library()
+    _need(plan, "plan", torch.int32, 2)
+    if plan.shape[1] != 2:
+        raise ValueError("plan must be (num_items, 2)")
+    out, lse, B, total_q, total_k, Hq, Hkv, d, scale = _varlen_args(
+        q, k, v, cu_seqlens_q, cu_seqlens_k, softmax_scale, out, lse, return_lse)
+    st = lib.fa_fwd_varlen_run(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                               _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(plan),
+                               plan.shape[0], B, int(max_seqlen_q), int(max_seqlen_k), total_q,
+                               total_k, Hq, Hkv, d, scale, int(bool(causal)), int(window[0]),
+                               int(window[1]), *_mods(softcap, alibi_slopes, B, Hq),
+                               _stream(stream))
+    _check("fa_fwd_varlen_run", st)
+    return out, lse
+
+
 def fa_decode_paged_workspace_size(B, Hq, d, max_blocks_per_seq, page_size, split_tokens=0):
     return int(load_library().fa_decode_paged_workspace_size(B, Hq, d, max_blocks_per_seq,
                                                               page_size, split_tokens))
 
 
-def fa_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale=None,
-                    window_left=-1, split_tokens=0, out=None, lse=None, workspace=None,
-                    return_lse=True, stream=None):
-    """Paged decode: q (B, 1, Hq, d), caches [num_pages, page_size, Hkv, d],
-    block_table int32 [B, max_blocks], cache_seqlens int32 [B] -> O, LSE (B, Hq)."""
+def _decode_args(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, split_tokens,
+                 out, lse, workspace, return_lse):
     torch = _torch()
-    lib = load_library()
     _need(q, "q", torch.bfloat16, 4)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     _need(v_cache, "v_cache", torch.bfloat16, 4)
@@ -239,12 +295,66 @@ def fa_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, softmax_sca
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    return out, lse, workspace, B, Hq, Hkv, d, num_pages, page_size, max_blocks, scale
+
+
+def fa_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale=None,
+                    window_left=-1, split_tokens=0, out=None, lse=None, workspace=None,
+                    return_lse=True, stream=None):
+    """Paged decode: q (B, 1, Hq, d), caches [num_pages, page_size, Hkv, d],
+    block_table int32 [B, max_blocks], cache_seqlens int32 [B] -> O, LSE (B, Hq)."""
+    lib = load_library()
+    out, lse, workspace, B, Hq, Hkv, d, num_pages, page_size, max_blocks, scale = _decode_args(
+        q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, split_tokens, out, lse,
+        workspace, return_lse)
     st = lib.fa_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                              _ptr(cache_seqlens), _ptr(out), _ptr(lse), B, Hq, Hkv, d, num_pages,
                              page_size, max_blocks, scale, int(window_left), int(split_tokens),
                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(stream))
     _check("fa_decode_paged", st)
+    return out, lse
+
+
+def fa_decode_plan(cache_seqlens, page_size, max_blocks_per_seq, window_left=-1, split_tokens=0):
+    """Host plan for fa_decode_paged_run from HOST lengths (list, numpy array or CPU tensor of
+    B ints) -> numpy int32 array (num_items, 2) of (request, split), heaviest first.  No GPU is
+    needed."""
+    import numpy as np
+    lib = load_library()
+    sl = np.ascontiguousarray(np.asarray(cache_seqlens, dtype=np.int64)).astype(np.int32)
+    if sl.ndim != 1 or sl.size < 1:
+        raise ValueError("cache_seqlens must be 1-D with at least one request")
+    n = ctypes.c_int(0)
+    args = (sl.ctypes.data_as(ctypes.c_void_p), sl.size, int(page_size), int(max_blocks_per_seq),
+            int(window_left), int(split_tokens))
+    _check("fa_decode_plan", lib.fa_decode_plan(*args, None, 0, ctypes.byref(n)))
+    plan = np.zeros((max(n.value, 1), 2), dtype=np.int32)
+    _check("fa_decode_plan", lib.fa_decode_plan(*args, plan.ctypes.data_as(ctypes.c_void_p),
+                                                 n.value, ctypes.byref(n)))
+    return plan[:n.value]
+
+
+def fa_decode_paged_run(q, k_cache, v_cache, block_table, cache_seqlens, plan,
+                        softmax_scale=None, window_left=-1, split_tokens=0, out=None, lse=None,
+                        workspace=None, return_lse=True, stream=None):
+    """fa_decode_paged over the items of a plan from fa_decode_plan (same lengths, page size,
+    block-table width, window and split size), uploaded as a device int32 tensor
+    (num_items, 2)."""
+    torch = _torch()
+    lib = load_library()
+    _need(plan, "plan", torch.int32, 2)
+    if plan.shape[1] != 2:
+        raise ValueError("plan must be (num_items, 2)")
+    out, lse, workspace, B, Hq, Hkv, d, num_pages, page_size, max_blocks, scale = _decode_args(
+        q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, split_tokens, out, lse,
+        workspace, return_lse)
+    st = lib.fa_decode_paged_run(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                 _ptr(cache_seqlens), _ptr(plan), plan.shape[0], _ptr(out),
+                                 _ptr(lse), B, Hq, Hkv, d, num_pages, page_size, max_blocks,
+                                 scale, int(window_left), int(split_tokens), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("fa_decode_paged_run", st)
     return out, lse
 
 
@@ -292,7 +402,8 @@ def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, 
     return out, lse
 
 
-__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_decode_paged", "fa_decode_paged_workspace_size",
-           "fa_fwd_kvcache",
+__all__ = ["fa_fwd", "fa_fwd_varlen", "fa_varlen_plan", "fa_fwd_varlen_run",
+           "fa_decode_paged", "fa_decode_plan", "fa_decode_paged_run",
+           "fa_decode_paged_workspace_size", "fa_fwd_kvcache",
            "load_library", "exported_symbols", "cu_seqlens_from_lengths",
            "lengths_from_cu_seqlens", "FAError", "LIB_PATH"]

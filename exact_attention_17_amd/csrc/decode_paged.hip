@@ -68,9 +68,25 @@ void decode_split_kernel(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // grid = (KV head x head subgroup, split, request): the workgroups of all KV
   // heads of one split are dispatched together, so the heads interleaved in
-  // each cache page are read at the same time (DRAM row locality).
-  const int s = blockIdx.y, b = blockIdx.z;
-  const int kvh = blockIdx.x / p.sub_groups, sub = blockIdx.x % p.sub_groups;
+  // each cache page are read at the same time (DRAM row locality).  With a
+  // host plan the grid is 1-D, (KV head x head subgroup) fastest, and the
+  // plan's item names the (request, split).
+  int s, b, gx;
+  if (p.planned) {
+    const int per = p.Hkv * p.sub_groups;
+    const int item = blockIdx.x / per;
+    gx = blockIdx.x - item * per;
+    const __attribute__((address_space(4))) int* pc =
+        (const __attribute__((address_space(4))) int*)p.plan;
+    b = pc[2 * item];
+    s = pc[2 * item + 1];
+    if (b < 0 || b >= p.B || s < 0 || s >= p.max_splits) return;   // not an item of this batch
+  } else {
+    s = blockIdx.y;
+    b = blockIdx.z;
+    gx = blockIdx.x;
+  }
+  const int kvh = gx / p.sub_groups, sub = gx % p.sub_groups;
   const int h0 = kvh * p.group + sub * GR;
   const int nrow = min(GR, p.group - sub * GR);
 
@@ -367,7 +383,9 @@ void decode_merge_kernel(DecodeParams p) {
 
 template <int D, bool PAGE16>
 static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
-  const dim3 grid(p.Hkv * p.sub_groups, p.max_splits, p.B), block(kDecodeThreads);
+  const dim3 grid = p.planned ? dim3(p.num_items * p.Hkv * p.sub_groups)
+                           : dim3(p.Hkv * p.sub_groups, p.max_splits, p.B);
+  const dim3 block(kDecodeThreads);
   switch (rows) {
     case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1, PAGE16>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2, PAGE16>), grid, block, 0, stream, p); break;
@@ -378,10 +396,13 @@ static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p, int rows, hipStream_t stream) {
-  if (p.page_size % 16 == 0) launch_split<D, true>(p, rows, stream);
-  else launch_split<D, false>(p, rows, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // an empty plan (every request has length 0): the merge alone writes O = 0
+  if (!p.planned || p.num_items > 0) {
+    if (p.page_size % 16 == 0) launch_split<D, true>(p, rows, stream);
+    else launch_split<D, false>(p, rows, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid2(p.Hq, p.B), block2(64);
   hipLaunchKernelGGL((decode_merge_kernel<D>), grid2, block2, 0, stream, p);
   return hipGetLastError();

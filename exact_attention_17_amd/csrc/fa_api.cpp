@@ -115,12 +115,18 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
-                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
-                        int Hq, int Hkv, int d, float softmax_scale, int causal,
-                        int window_left, int window_right, float softcap,
-                        const float* alibi_slopes, int alibi_batch_stride, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_fwd_varlen and fa_fwd_varlen_run: plan = NULL walks the tiles in
+// sequence order, else the kernel takes its items from the plan.
+fa_status varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k, const int* plan,
+                      int num_items, int B, int max_seqlen_q, int max_seqlen_k, int total_q,
+                      int total_k, int Hq, int Hkv, int d, float softmax_scale, int causal,
+                      int window_left, int window_right, float softcap,
+                      const float* alibi_slopes, int alibi_batch_stride, void* stream) {
   fa_status st = check_common(Hq, Hkv, d, softmax_scale, causal, window_left, window_right);
   if (st != FA_OK) return st;
   if ((st = check_tensors(q, k, v, o, lse)) != FA_OK) return st;
@@ -151,12 +157,51 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   p.scale_log2 = softmax_scale * kLog2e;
   p.causal = causal; p.win_left = window_left; p.win_right = window_right;
   set_mods(p, softmax_scale, softcap, alibi_slopes, alibi_batch_stride);
-  // tile slots: sequence b owns [cu_q[b]/128 + b, cu_q[b+1]/128 + b + 1)
-  p.num_q_tiles = total_q / fa::kBlockM + B;
+  if (plan) {
+    p.plan = plan;
+    p.num_q_tiles = num_items;
+  } else {
+    // tile slots: sequence b owns [cu_q[b]/128 + b, cu_q[b+1]/128 + b + 1)
+    p.num_q_tiles = total_q / fa::kBlockM + B;
+  }
   p.xcd_groups = xcd_groups(Hkv);
   if ((int64_t)p.num_q_tiles * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
+  if (p.num_q_tiles == 0) return FA_OK;
   hipError_t e = fa::launch_prefill(p, d, 1, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                        int Hq, int Hkv, int d, float softmax_scale, int causal,
+                        int window_left, int window_right, float softcap,
+                        const float* alibi_slopes, int alibi_batch_stride, void* stream) {
+  return varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nullptr, 0, B, max_seqlen_q,
+                     max_seqlen_k, total_q, total_k, Hq, Hkv, d, softmax_scale, causal,
+                     window_left, window_right, softcap, alibi_slopes, alibi_batch_stride, stream);
+}
+
+fa_status fa_fwd_varlen_run(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* cu_seqlens_q, const int* cu_seqlens_k, const int* plan,
+                            int num_items, int B, int max_seqlen_q, int max_seqlen_k,
+                            int total_q, int total_k, int Hq, int Hkv, int d,
+                            float softmax_scale, int causal, int window_left, int window_right,
+                            float softcap, const float* alibi_slopes, int alibi_batch_stride,
+                            void* stream) {
+  if (num_items < 0 || (num_items > 0 && (!plan || !aligned(plan, 8)))) return FA_ERR_INVALID_ARG;
+  // one item per query tile: a plan for these lengths has between 1 (when
+  // total_q > 0) and total_q / 128 + B items; an empty plan may be NULL
+  if ((int64_t)num_items > (int64_t)total_q / fa::kBlockM + B) return FA_ERR_INVALID_ARG;
+  if (total_q > 0 && num_items == 0) return FA_ERR_INVALID_ARG;
+  return varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, plan, num_items, B,
+                     max_seqlen_q, max_seqlen_k, total_q, total_k, Hq, Hkv, d, softmax_scale,
+                     causal, window_left, window_right, softcap, alibi_slopes,
+                     alibi_batch_stride, stream);
 }
 
 fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
@@ -256,12 +301,18 @@ size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_blocks_per_s
   return part_o_bytes(B, Hq, d, max_splits) + lse_bytes;
 }
 
-fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                          const int* block_table, const int* cache_seqlens,
-                          void* o, float* lse, int B, int Hq, int Hkv, int d,
-                          int num_pages, int page_size, int max_blocks_per_seq,
-                          float softmax_scale, int window_left, int split_tokens,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_decode_paged and fa_decode_paged_run: plan = NULL launches every
+// (request, split) slot, else only the plan's items.
+fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                      const int* block_table, const int* cache_seqlens, bool planned,
+                      const int* plan, int num_items, void* o, float* lse, int B, int Hq, int Hkv, int d,
+                      int num_pages, int page_size, int max_blocks_per_seq,
+                      float softmax_scale, int window_left, int split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   fa_status st = check_common(Hq, Hkv, d, softmax_scale, 0, window_left, -1);
   if (st != FA_OK) return st;
   if ((st = check_tensors(q, k_cache, v_cache, o, lse)) != FA_OK) return st;
@@ -273,10 +324,21 @@ fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cach
   if (B > 65535 || cdiv((int64_t)max_blocks_per_seq * page_size, effective_split(split_tokens)) > 65535)
     return FA_ERR_INVALID_ARG;
   if ((int64_t)num_pages * page_size * Hkv * d >= ((int64_t)1 << 40)) return FA_ERR_INVALID_ARG;
+  const int split = effective_split(split_tokens);
+  const int max_splits = (int)cdiv((int64_t)max_blocks_per_seq * page_size, split);
+  const int rows = pow2_rows(Hq / Hkv);
+  const int sub_groups = (int)cdiv(Hq / Hkv, rows);
+  if (planned) {
+    // planned grid: one 1-D launch of num_items * Hkv * sub_groups workgroups;
+    // an empty plan (every request empty) may be NULL
+    if (num_items < 0 || (int64_t)num_items > (int64_t)B * max_splits) return FA_ERR_INVALID_ARG;
+    if (num_items > 0 && (!plan || !aligned(plan, 8))) return FA_ERR_INVALID_ARG;
+    if ((int64_t)num_items * Hkv * sub_groups * fa::kDecodeThreads >= ((int64_t)1 << 32))
+      return FA_ERR_INVALID_ARG;
+  }
   const size_t need = fa_decode_paged_workspace_size(B, Hq, d, max_blocks_per_seq, page_size, split_tokens);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return FA_ERR_WORKSPACE;
 
-  const int split = effective_split(split_tokens);
   fa::DecodeParams p = {};
   p.q = static_cast<const uint16_t*>(q);
   p.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -286,18 +348,46 @@ fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cach
   p.o = static_cast<uint16_t*>(o);
   p.lse = lse;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
-  const int rows = pow2_rows(p.group);
-  p.sub_groups = (int)cdiv(p.group, rows);
+  p.sub_groups = sub_groups;
   p.page_size = page_size;
   p.max_blocks = max_blocks_per_seq;
   p.split_tokens = split;
-  p.max_splits = (int)cdiv((int64_t)max_blocks_per_seq * page_size, split);
+  p.max_splits = max_splits;
   p.part_o = static_cast<float*>(workspace);
   p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_o_bytes(B, Hq, d, p.max_splits));
   p.scale_log2 = softmax_scale * kLog2e;
   p.win_left = window_left;
+  p.planned = planned;
+  p.plan = plan;
+  p.num_items = num_items;
   hipError_t e = fa::launch_decode(p, d, rows, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                          const int* block_table, const int* cache_seqlens,
+                          void* o, float* lse, int B, int Hq, int Hkv, int d,
+                          int num_pages, int page_size, int max_blocks_per_seq,
+                          float softmax_scale, int window_left, int split_tokens,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, block_table, cache_seqlens, false, nullptr, 0, o, lse, B, Hq,
+                     Hkv, d, num_pages, page_size, max_blocks_per_seq, softmax_scale,
+                     window_left, split_tokens, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_decode_paged_run(const void* q, const void* k_cache, const void* v_cache,
+                              const int* block_table, const int* cache_seqlens, const int* plan,
+                              int num_items, void* o, float* lse, int B, int Hq, int Hkv, int d,
+                              int num_pages, int page_size, int max_blocks_per_seq,
+                              float softmax_scale, int window_left, int split_tokens,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, block_table, cache_seqlens, true, plan, num_items, o, lse, B,
+                     Hq, Hkv, d, num_pages, page_size, max_blocks_per_seq, softmax_scale,
+                     window_left, split_tokens, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -28,6 +28,7 @@ struct PrefillParams {
   float* lse;              // may be null
   const int* cu_q;         // varlen only
   const int* cu_k;
+  const int* plan;         // varlen only, may be null: (b, query tile) pairs in run order
   int B, Lq, Lk;           // dense: lengths; varlen: Lq/Lk unused
   int Hq, Hkv, group;      // group = Hq / Hkv
   int64_t q_tok_stride;    // elements between consecutive tokens = H*d
@@ -37,7 +38,7 @@ struct PrefillParams {
   int lse_seq_stride;      // dense: Lq (lse is (B, Hq, Lq)); varlen: total_q
   float scale_log2;        // softmax_scale * log2(e)
   int causal, win_left, win_right;
-  int num_q_tiles;         // dense: ceil(Lq / kBlockM); varlen: total tile slots
+  int num_q_tiles;         // dense: ceil(Lq / kBlockM); varlen: tile slots or plan items
   int xcd_groups;          // >0: XCD-aware work mapping with this many KV groups
   int chunk_groups;        // KV groups an XCD works on together (dense mapping)
   // paged KV cache (chunked prefill): k/v are the page pools
@@ -78,6 +79,9 @@ struct DecodeParams {
   int page_size, max_blocks, split_tokens, max_splits;
   float scale_log2;
   int win_left;
+  bool planned;            // false: grid over every (split, request) slot
+  const int* plan;         // planned: (request, split) pairs, one per item
+  int num_items;
 };
 
 // mode: 0 dense, 1 varlen, 2 paged KV cache

@@ -18,7 +18,8 @@
  * Conventions shared by every entry point
  *   - Element type of q, k, v, o, caches: bfloat16, row-major, contiguous,
  *     last dimension (head_dim) has stride 1.  lse: float32, natural log.
- *   - All pointers except `stream` are DEVICE pointers owned by the caller;
+ *   - All pointers except `stream` and those of fa_varlen_plan (host memory)
+ *     are DEVICE pointers owned by the caller;
  *     the library never allocates, frees, synchronises or keeps a pointer
  *     after the call returns.  q/k/v/o/cache pointers must be 16-byte
  *     aligned.  `lse` may be NULL (then no LSE is written).
@@ -105,6 +106,49 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         const float* alibi_slopes, int alibi_batch_stride, void* stream);
 
 /*
+ * Plan / run split for varlen prefill ("FIA / FlashAttention" explainer,
+ * sec. 2: FlashInfer's plan step balances the load of variable-length
+ * batches on the host, then a run step executes the batch).
+ *
+ * fa_varlen_plan is pure host code (no HIP call).  From HOST copies of the
+ * cumulative lengths it lists the work items of fa_fwd_varlen_run -- one per
+ * query tile of 128 rows, (sequence b, tile index) as two int32 -- ordered
+ * by the number of key tiles each one visits under the given causal flag and
+ * window, heaviest first (ties keep sequence order), so that long items start
+ * early and short ones fill the end of the launch.
+ *   cu_seqlens_q, cu_seqlens_k : host int32 arrays of B+1 offsets, as for
+ *       fa_fwd_varlen (non-decreasing, cu[0] = 0; checked here).
+ *   plan : host int32 array of 2 * plan_capacity, or NULL to only count.
+ *   num_items : out, the number of items (sum over b of ceil(Lq_b / 128)).
+ * Returns FA_ERR_WORKSPACE if plan_capacity < *num_items (then *num_items
+ * is still set and plan is untouched), FA_ERR_INVALID_ARG for bad lengths.
+ *
+ * fa_fwd_varlen_run computes exactly what fa_fwd_varlen computes (bit for
+ * bit: every tile runs the same code) in the order of a plan uploaded by the
+ * caller to device memory.  Arguments are those of fa_fwd_varlen plus
+ *   plan : device int32 array of 2 * num_items, 8-byte aligned, made by
+ *       fa_varlen_plan for these cu_seqlens, causal flag and window (may be
+ *       NULL when num_items is 0);
+ *   num_items : its item count (1 .. total_q / 128 + B when total_q > 0;
+ *       0 when total_q is 0).
+ * The run computes only the listed tiles: rows of a tile missing from the
+ * plan are not written; an item naming a sequence or tile that does not
+ * exist is skipped.  A plan can be reused for every call with the same
+ * lengths, mask and window.
+ */
+fa_status fa_varlen_plan(const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int causal,
+                         int window_left, int window_right, int* plan, int plan_capacity,
+                         int* num_items);
+
+fa_status fa_fwd_varlen_run(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* cu_seqlens_q, const int* cu_seqlens_k, const int* plan,
+                            int num_items, int B, int max_seqlen_q, int max_seqlen_k,
+                            int total_q, int total_k, int Hq, int Hkv, int d,
+                            float softmax_scale, int causal, int window_left, int window_right,
+                            float softcap, const float* alibi_slopes, int alibi_batch_stride,
+                            void* stream);
+
+/*
  * Bytes of device workspace fa_decode_paged needs for these sizes (split
  * partials: one float32 row of d values plus one float32 LSE per request,
  * query head and split).  split_tokens = 0 selects the default of 512.
@@ -141,6 +185,51 @@ fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cach
                           int num_pages, int page_size, int max_blocks_per_seq,
                           float softmax_scale, int window_left, int split_tokens,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Plan / run split for paged decode ("FIA / FlashAttention" explainer,
+ * sec. 2 and its batch-decode example: a plan object is made on the host,
+ * then the batched decode runs with it).
+ *
+ * fa_decode_plan is pure host code (no HIP call).  From a HOST copy of
+ * cache_seqlens it lists the (request b, split s) pairs that hold at least
+ * one visible key -- split s covers keys [s * split_tokens, (s+1) *
+ * split_tokens), and with window_left >= 0 only the last window_left + 1
+ * keys are visible -- as two int32 each, ordered by the number of keys they
+ * read, heaviest first (ties keep request order).  Arguments as for
+ * fa_decode_paged; it also checks 0 <= cache_seqlens[b] <=
+ * max_blocks_per_seq * page_size on the host.
+ *   plan : host int32 array of 2 * plan_capacity, or NULL to only count.
+ *   num_items : out, the number of items.
+ * Returns FA_ERR_WORKSPACE if plan_capacity < *num_items (then *num_items
+ * is still set and plan is untouched), FA_ERR_INVALID_ARG for bad sizes.
+ *
+ * fa_decode_paged_run computes what fa_decode_paged computes (bit for bit:
+ * every split runs the same code and the merge is the same kernel) but
+ * launches one workgroup per plan item and KV head (group) instead of one
+ * per (request, split slot), so no workgroup starts without keys to read.
+ * Arguments are those of fa_decode_paged plus
+ *   plan : device int32 array of 2 * num_items, 8-byte aligned, made by
+ *       fa_decode_plan for the same cache_seqlens, page_size,
+ *       max_blocks_per_seq, window_left and split_tokens (may be NULL when
+ *       num_items is 0);
+ *   num_items : its item count (0 .. B * number of split slots).
+ * The plan must be complete: the merge reads the partial result of every
+ * split that holds a visible key, and a split missing from the plan leaves
+ * its workspace slot as it was (the output is then undefined, though no
+ * memory outside the buffers is touched).  Items naming a request or split
+ * that does not exist are skipped.
+ */
+fa_status fa_decode_plan(const int* cache_seqlens, int B, int page_size, int max_blocks_per_seq,
+                         int window_left, int split_tokens, int* plan, int plan_capacity,
+                         int* num_items);
+
+fa_status fa_decode_paged_run(const void* q, const void* k_cache, const void* v_cache,
+                              const int* block_table, const int* cache_seqlens, const int* plan,
+                              int num_items, void* o, float* lse, int B, int Hq, int Hkv, int d,
+                              int num_pages, int page_size, int max_blocks_per_seq,
+                              float softmax_scale, int window_left, int split_tokens,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Attention of Lq new query tokens per request over a paged KV cache

@@ -33,8 +33,10 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert names == sorted(["fa_status_string", "fa_fwd", "fa_fwd_varlen",
-                            "fa_decode_paged_workspace_size", "fa_decode_paged", "fa_fwd_kvcache"])
+    assert names == sorted(["fa_status_string", "fa_fwd", "fa_fwd_varlen", "fa_varlen_plan",
+                            "fa_fwd_varlen_run", "fa_decode_paged_workspace_size",
+                            "fa_decode_paged", "fa_decode_plan", "fa_decode_paged_run",
+                            "fa_fwd_kvcache"])
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(fa.exported_symbols()) == names
@@ -89,6 +91,33 @@ def test_varlen_rejects(lib, kw, code):
     assert varlen(lib, **kw) == code
 
 
+def varlen_run(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, cq=P, ck=P, plan=P, n=2, B=2, mq=10, mk=10, tq=16,
+             tk=16, Hq=4, Hkv=2, d=128, scale=0.1, causal=1, wl=-1, wr=-1, cap=0.0, al=None, ab=0)
+    a.update(kw)
+    return lib.fa_fwd_varlen_run(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
+                                 a["plan"], a["n"], a["B"], a["mq"], a["mk"], a["tq"], a["tk"],
+                                 a["Hq"], a["Hkv"], a["d"], a["scale"], a["causal"], a["wl"],
+                                 a["wr"], a["cap"], a["al"], a["ab"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(plan=None), INVALID), (dict(plan=P + 4), INVALID), (dict(n=-1), INVALID),
+    (dict(n=0), INVALID), (dict(n=0, plan=None), INVALID), (dict(n=3), INVALID),
+    (dict(tq=300, mq=300, n=5), INVALID),
+    (dict(cq=None), INVALID), (dict(mq=20), INVALID), (dict(d=80), UNSUPPORTED),
+    (dict(Hq=5), INVALID), (dict(cap=-0.5), INVALID), (dict(al=P, ab=3), INVALID),
+])
+def test_varlen_run_rejects(lib, kw, code):
+    assert varlen_run(lib, **kw) == code
+
+
+def test_varlen_run_empty_batch_is_a_noop(lib):
+    # total_q = 0: nothing to compute, so no plan item and no launch
+    assert varlen_run(lib, tq=0, mq=0, n=0) == OK
+    assert varlen_run(lib, tq=0, mq=0, n=0, plan=None) == OK
+
+
 def test_varlen_empty_batch_is_a_no_op(lib):
     assert varlen(lib, tq=0, mq=0) == OK
 
@@ -126,6 +155,27 @@ def decode(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
+
+
+def decode_run(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, bt=P, sl=P, plan=P, n=4, o=P, lse=P, B=4, Hq=8, Hkv=2, d=128,
+             pages=64, ps=16, mb=8, scale=0.1, wl=-1, split=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.fa_decode_paged_run(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["plan"], a["n"],
+                                   a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                   a["pages"], a["ps"], a["mb"], a["scale"], a["wl"], a["split"],
+                                   a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(plan=None), INVALID), (dict(plan=P + 4), INVALID), (dict(n=-1), INVALID),
+    # 8 blocks of 16 tokens = 128 keys = one 512-token split per request: at most B items
+    (dict(n=5), INVALID), (dict(split=16, n=33), INVALID),
+    (dict(bt=None), INVALID), (dict(split=24), INVALID), (dict(d=32), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE),
+])
+def test_decode_run_rejects(lib, kw, code):
+    assert decode_run(lib, **kw) == code
 
 
 def kvcache(lib, **kw):

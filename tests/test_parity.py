@@ -3,7 +3,8 @@
 Small cases are compared element by element over every output; they span
 several 128-row / 64-key tiles with ragged tails and cover each mask mode,
 MHA/GQA/MQA, both head dims, Lq != Lk, fully masked rows, zero-length varlen
-sequences and paged layouts with several page sizes and split sizes.  The five
+sequences, plans in heaviest-first, shuffled and partial order, and paged
+layouts with several page sizes and split sizes.  The five
 named workloads run at full size in the launch configuration bench.py times;
 prefill outputs are checked on sampled rows the oracle computes one by one,
 the decode workload on every output.
@@ -146,6 +147,102 @@ def test_decode_sweep(fa, case):
     check(f"decode{case}", o, lse, O, LSE)
 
 
+def run_decode_planned(fa, w, plan=None):
+    max_blocks = w.block_table.shape[1]
+    if plan is None:
+        plan = fa.fa_decode_plan(w.seqlens, w.page_size, max_blocks, w.window_left, w.split_tokens)
+    out = fa.fa_decode_paged_run(dev(w.q), dev(w.k_cache), dev(w.v_cache),
+                                 dev(torch.from_numpy(w.block_table)),
+                                 dev(torch.from_numpy(w.seqlens)),
+                                 dev(torch.from_numpy(np.ascontiguousarray(plan).reshape(-1, 2))),
+                                 w.scale, w.window_left, w.split_tokens)
+    torch.cuda.synchronize()
+    return out[0].cpu(), out[1].cpu()
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"n{len(c[0])}-h{c[1]}-kv{c[2]}-d{c[3]}-p{c[4]}-s{c[5]}-w{c[6]}")
+def test_decode_run_sweep(fa, case):
+    lens, Hq, Hkv, d, ps, split, wl = case
+    npages = sum(-(-l // ps) for l in lens) + 3
+    w = workloads.random_paged(300 + sum(lens) + ps, lens, Hq, Hkv, d, ps, npages, split,
+                               max_blocks=max(1, -(-max(lens) // ps)) + 2, window_left=wl)
+    o, lse = run_decode_planned(fa, w)
+    O, LSE = decode_ref(w)
+    check(f"decode run{case}", o, lse, O, LSE)
+    o2, lse2 = run_decode(fa, w)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+
+
+def test_decode_run_any_order_and_empty_plan(fa):
+    w = workloads.random_paged(977, [1000, 3, 513], 8, 2, 128, 16, 200, 256, max_blocks=70)
+    plan = fa.fa_decode_plan(w.seqlens, 16, 70, -1, 256)
+    ref = run_decode_planned(fa, w, plan)
+    shuffled = plan[np.random.default_rng(3).permutation(len(plan))]
+    o, lse = run_decode_planned(fa, w, shuffled)
+    assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16)) and torch.equal(lse, ref[1])
+    # every request empty: the plan has no item and the merge alone writes O = 0, LSE = -inf
+    e = workloads.random_paged(978, [0, 0], 4, 2, 128, 16, 8, 512, max_blocks=4)
+    plan = fa.fa_decode_plan(e.seqlens, 16, 4, -1, 512)
+    assert plan.shape == (0, 2)
+    o, lse = run_decode_planned(fa, e, plan)
+    assert (o.float() == 0).all() and torch.isneginf(lse).all()
+
+
+# ------------------------------------------------- varlen plan / run split
+def run_planned(fa, w, plan=None, out=None, lse=None):
+    if plan is None:
+        plan = fa.fa_varlen_plan(w.cu_seqlens, w.cu_seqlens, w.causal, w.window)
+    cu = dev(torch.from_numpy(w.cu_seqlens))
+    o, l = fa.fa_fwd_varlen_run(dev(w.q), dev(w.k), dev(w.v), cu, cu,
+                                dev(torch.from_numpy(np.ascontiguousarray(plan))),
+                                w.max_seqlen, w.max_seqlen, w.scale, w.causal, w.window,
+                                out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o.cpu(), l.cpu()
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: f"n{len(c[0])}-h{c[1]}-kv{c[2]}-d{c[3]}-c{int(c[4])}-w{c[5][0]}")
+def test_varlen_run_sweep(fa, case):
+    lens, Hq, Hkv, d, causal, window = case
+    w = workloads.random_varlen(200 + sum(lens) + d, lens, Hq, Hkv, d, causal, window)
+    o, lse = run_planned(fa, w)
+    O, LSE = oracle.attention_varlen_ref(bits(w.q), bits(w.k), bits(w.v), w.cu_seqlens,
+                                         w.cu_seqlens, w.scale, causal, window)
+    check(f"varlen run{case}", o, lse, O, LSE)
+    # the same tiles run the same code: identical bits to the unplanned call
+    cu = dev(torch.from_numpy(w.cu_seqlens))
+    o2, lse2 = fa.fa_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), cu, cu, w.max_seqlen,
+                                w.max_seqlen, w.scale, causal, window)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.cpu().view(torch.int16))
+    assert torch.equal(lse, lse2.cpu())
+
+
+def test_varlen_run_any_order_and_partial_plans(fa):
+    w = workloads.random_varlen(911, [300, 5, 0, 200, 129], 4, 2, 128, True, (100, 0))
+    plan = fa.fa_varlen_plan(w.cu_seqlens, w.cu_seqlens, w.causal, w.window)
+    ref_o, ref_l = run_planned(fa, w, plan)
+    rng = np.random.default_rng(7)
+    o, l = run_planned(fa, w, plan[rng.permutation(len(plan))])
+    assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(l, ref_l)
+    # a partial plan with items that name no tile: listed tiles are computed,
+    # unlisted rows keep the caller's values, bad items are skipped
+    keep = plan[::2]
+    bad = np.array([[5, 0], [-1, 0], [0, 3], [1, -1], [3, 2]], dtype=np.int32)
+    part = np.concatenate([keep, bad])
+    sent_o = torch.full_like(w.q, 7.0, device="cuda")
+    sent_l = torch.full((w.q.shape[1], w.q.shape[0]), 7.0, dtype=torch.float32, device="cuda")
+    o, l = run_planned(fa, w, part, out=sent_o, lse=sent_l)
+    listed = np.zeros(w.q.shape[0], dtype=bool)
+    for b, t in keep.tolist():
+        s0 = int(w.cu_seqlens[b]) + 128 * t
+        listed[s0:min(s0 + 128, int(w.cu_seqlens[b + 1]))] = True
+    idx = torch.from_numpy(listed)
+    assert torch.equal(o[idx].view(torch.int16), ref_o[idx].view(torch.int16))
+    assert torch.equal(l[:, idx], ref_l[:, idx])
+    assert (o[~idx] == 7.0).all() and (l[:, ~idx] == 7.0).all()
+
+
 # ---------------------------------------------------------- full workloads
 def sampled_rows(L, rng, extra=12):
     fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, L // 2, L - 129, L - 128, L - 2, L - 1]
@@ -185,19 +282,24 @@ def test_full_causal_gqa_long(fa):
     check_dense_sampled(w.name, w, o, lse, pairs, rng)
 
 
-def test_full_paged_decode(fa):
+@pytest.mark.parametrize("planned", [False, True], ids=["all_split_slots", "planned"])
+def test_full_paged_decode(fa, planned):
     w = workloads.paged_decode()
-    o, lse = run_decode(fa, w)
+    o, lse = run_decode_planned(fa, w) if planned else run_decode(fa, w)
     O, LSE = decode_ref(w)
     check(w.name, o, lse, O, LSE)
 
 
-def test_full_varlen_window(fa):
+@pytest.mark.parametrize("planned", [False, True], ids=["sequence_order", "planned"])
+def test_full_varlen_window(fa, planned):
     w = workloads.varlen_window()
     cu = dev(torch.from_numpy(w.cu_seqlens))
-    o, lse = fa.fa_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), cu, cu, w.max_seqlen, w.max_seqlen,
-                              w.scale, w.causal, w.window)
-    torch.cuda.synchronize()
+    if planned:
+        o, lse = run_planned(fa, w)
+    else:
+        o, lse = fa.fa_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), cu, cu, w.max_seqlen,
+                                  w.max_seqlen, w.scale, w.causal, w.window)
+        torch.cuda.synchronize()
     o, lse = f64(o.cpu()), f64(lse.cpu())
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     qb, kb, vb = bits(w.q), bits(w.k), bits(w.v)

@@ -177,13 +177,22 @@ def paged_decode(seed=4, batch=64, Hq=32, Hkv=8, d=128, page_size=16, pool_pages
 
 
 # ---------------------------------------------------------------- workload 5
+def _log_uniform_lengths(rng, nseq, lo, hi):
+    return np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), size=nseq))).astype(np.int32)
+
+
+def varlen_window_lengths(seed=5, nseq=16, lo=64, hi=8192):
+    """The sequence lengths varlen_window draws (first draw of the same seed)."""
+    return _log_uniform_lengths(np.random.default_rng(seed), nseq, lo, hi)
+
+
 def varlen_window(seed=5, nseq=16, H=16, d=64, lo=64, hi=8192, window=(4096, 0)):
     """Varlen packed causal prefill with a sliding window: 16 sequences with
     lengths log-uniform in [64, 8192] (rint(exp(U(ln lo, ln hi)))), packed with
     cu_seqlens and no padding, H=16, d=64, window (4096, 0).
     Draw order: lengths; q; k; v."""
     rng = np.random.default_rng(seed)
-    lens = np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), size=nseq))).astype(np.int32)
+    lens = _log_uniform_lengths(rng, nseq, lo, hi)
     cu = np.zeros(nseq + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)
     T = int(cu[-1])
