@@ -32,12 +32,22 @@ Readings where the pages are silent (each listed in the design doc):
   cache_seqlens[b] + i; softcap acts on the scaled logits and the ALiBi bias,
   -slope * |i + Lk - Lq - j|, is added after it, both before the mask.
 
+Gradients (``backward.py``): the derivative of that definition for an
+upstream gradient dO, by the chain rule -- dV = P^T dO, dS = P * (dO V^T - D)
+with D_i = dO_i . O_i, dQ = scale dS K, dK = scale dS^T Q, summed over the
+query heads of a KV group.  The pages fix only that a fused backward
+recomputes the blocks from saved row statistics ("FlashAttention" concept
+page, recomputation; "FIA / FlashAttention" explainer, sec. 1); the values
+are those of the plain definition.
+
 Inputs are numpy arrays; a uint16 array is taken as bfloat16 bit patterns
 (numpy has no bfloat16 type) and converted exactly to float64.
 
-Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
-closed forms, invariants, a pure-Python brute force and PyTorch's CPU
-``scaled_dot_product_attention`` in float64.  No function is parity-unpinned.
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_backward_pins.py`` against closed forms, invariants, a
+pure-Python brute force, central finite differences, PyTorch's CPU
+``scaled_dot_product_attention`` and autograd in float64.  No function is
+parity-unpinned.
 """
 
 from .attention import (
@@ -55,6 +65,12 @@ from .attention import (
     merge_partials_ref,
     online_softmax_ref,
 )
+from .backward import (
+    attention_bwd_rows,
+    attention_bwd_ref,
+    attention_bwd_query_rows_ref,
+    attention_bwd_key_rows_ref,
+)
 
 __all__ = [
     "key_visibility",
@@ -70,4 +86,8 @@ __all__ = [
     "decode_split_partials_ref",
     "merge_partials_ref",
     "online_softmax_ref",
+    "attention_bwd_rows",
+    "attention_bwd_ref",
+    "attention_bwd_query_rows_ref",
+    "attention_bwd_key_rows_ref",
 ]
