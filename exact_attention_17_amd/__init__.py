@@ -44,6 +44,10 @@ _EXPORTS = {
                           + [ctypes.c_int] * 9 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int] + _MODS + [ctypes.c_void_p]),
     "fa_decode_paged_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 6),
+    "fa_bwd_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 3),
+    "fa_bwd": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6
+               + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fa_decode_plan": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_int] * 5
                        + [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
     "fa_decode_paged_run": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int]
@@ -358,6 +362,42 @@ def fa_decode_paged_run(q, k_cache, v_cache, block_table, cache_seqlens, plan,
     return out, lse
 
 
+def fa_bwd_workspace_size(B, Hq, Lq):
+    return int(load_library().fa_bwd_workspace_size(B, Hq, Lq))
+
+
+def fa_bwd(q, k, v, out, lse, dout, softmax_scale=None, causal=False, window=(-1, -1),
+           dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of fa_fwd: q, out, dout (B, Lq, Hq, d), k, v (B, Lk, Hkv, d) bf16, lse
+    (B, Hq, Lq) float32 from fa_fwd -> dq, dk, dv (bf16, shapes of q, k, v)."""
+    torch = _torch()
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, nm, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Lq, Hq, d = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Lk, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be (B, Lk, Hkv, d)")
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("out and dout must have q's shape")
+    if tuple(lse.shape) != (B, Hq, Lq):
+        raise ValueError("lse must be (B, Hq, Lq)")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        need = fa_bwd_workspace_size(B, Hq, Lq)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                    _ptr(dk), _ptr(dv), B, Lq, Lk, Hq, Hkv, d, scale, int(bool(causal)),
+                    int(window[0]), int(window[1]), _ptr(workspace),
+                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("fa_bwd", st)
+    return dq, dk, dv
+
+
 def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=None,
                    softmax_scale=None, causal=True, window=(-1, -1), out=None, lse=None,
                    return_lse=True, stream=None, softcap=0.0, alibi_slopes=None):
@@ -404,6 +444,7 @@ def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, 
 
 __all__ = ["fa_fwd", "fa_fwd_varlen", "fa_varlen_plan", "fa_fwd_varlen_run",
            "fa_decode_paged", "fa_decode_plan", "fa_decode_paged_run",
-           "fa_decode_paged_workspace_size", "fa_fwd_kvcache",
+           "fa_decode_paged_workspace_size", "fa_fwd_kvcache", "fa_bwd",
+           "fa_bwd_workspace_size",
            "load_library", "exported_symbols", "cu_seqlens_from_lengths",
            "lengths_from_cu_seqlens", "FAError", "LIB_PATH"]

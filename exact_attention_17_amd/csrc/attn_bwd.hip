@@ -1,0 +1,553 @@
+// Backward pass of fused exact attention for gfx950 (dense layout).
+//
+// What it computes: dQ, dK, dV of O = softmax(scale * Q K^T + mask) V (the
+// forward of prefill_fwd.hip) for an upstream gradient dO, by the chain rule
+// of that definition:
+//   P = exp(scale * Q K^T - LSE)       recomputed from the saved LSE
+//   dV = P^T dO,  dP = dO V^T,  delta_i = dO_i . O_i,  dS = P * (dP - delta)
+//   dQ = scale * dS K,  dK = scale * dS^T Q
+// with the dK, dV of a KV head summed over the query heads of its group.  The
+// pages' backward keeps no score matrix from the forward and recomputes the
+// blocks it needs from the saved row statistics ("FlashAttention" concept
+// page, recomputation; "FIA / FlashAttention" explainer, sec. 1).
+//
+// Mapping onto CDNA4 (our design, not the pages'):
+//   * bwd_prep_kernel: delta = dO . O and lse2 = LSE * log2(e) per query row,
+//     one coalesced pass over dO and O, into a caller workspace.
+//   * bwd_dkdv_kernel: a workgroup owns 128 keys of one (batch, KV head), 32
+//     per wave.  The wave's K and V rows stay in registers as MFMA B
+//     operands; its dK^T and dV^T accumulate in registers over every query
+//     row of every query head of the group, streamed through LDS in 64-row
+//     tiles.  Per 32-row half, S = Q K^T and dP = dO V^T take Q and dO rows
+//     from LDS as the A operand; the accumulator gives each lane one key and
+//     16 query rows, which rounded to bf16 are exactly the B operand of
+//     dV^T += dO^T P and dK^T += Q^T dS (A = dO^T and Q^T by transpose reads),
+//     so P and dS never leave registers.
+//   * bwd_dq_kernel: a workgroup owns 128 query rows of one (batch, head), 32
+//     per wave, as in the forward; the wave's Q and dO rows stay in registers
+//     as B operands while K and V stream through LDS in 64-key tiles:
+//     S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T (K^T by transpose
+//     reads).  Each lane holds one query row, so its lse2 and delta are two
+//     registers.
+//   * No atomics: every gradient element is summed by one wave in a fixed
+//     order, so the result is bitwise reproducible run to run.
+//   * Tiles go global -> LDS directly (buffer loads with the lds flag),
+//     double-buffered; one XOR swizzle serves both the row reads and the
+//     transpose reads of the same tile.
+#include "fa_internal.h"
+#include "gfx950.h"
+#include "work_map.h"
+
+#include <math.h>
+
+#include <type_traits>
+
+namespace fa {
+
+namespace {
+
+constexpr float kLog2eF = 1.4426950408889634f;
+
+// [64 rows][D] bf16 tiles, row-major and unpadded (each direct-to-LDS load
+// instruction writes 1 KB contiguously).  16-byte chunk c of row r is stored
+// at chunk c ^ swz(r), which depends on r & 15 only:
+//   D = 128: swz = 4 (r & 3) + ((r >> 2) & 3).  The 16 rows of a 16-row block
+//     get 16 distinct values, so a row read (lane n on row n, 16 bytes) puts
+//     16 lanes on 16 distinct 16-byte bank groups; the 4 rows of an aligned
+//     transpose-read group differ in bits 2-3, so their 4 x 4 chunks land on
+//     16 distinct bank groups.
+//   D = 64: swz = 4 ((r >> 1) & 1) + ((r >> 2) & 3).  Rows are 128 bytes, so
+//     rows of equal parity share a bank half: the 8 even (odd) rows of a
+//     16-row block get distinct values, and rows r and r + 2 of a transpose
+//     group differ in bit 2.
+template <int D> struct BLds {
+  static constexpr int kTile = 64 * D;
+  FA_DEV static int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+};
+
+// Float offset of row i's lse2 in the statistics of (b, h); its delta is 64
+// floats further.
+FA_DEV int64_t stat_offset(const BwdParams& p, int b, int h, int i) {
+  return ((int64_t)(b * p.Hq + h) * (p.Lq_pad / kBwdStatRows) + i / kBwdStatRows) *
+             (2 * kBwdStatRows) + (i % kBwdStatRows);
+}
+
+}  // namespace
+
+// One group of D/8 lanes per (batch, row, head), rows padded to Lq_pad:
+// delta = sum_d dO * O in fp32 (fixed order), lse2 = LSE * log2(e), or +inf
+// for a row with no visible key (LSE = -inf) and for padding rows, so that
+// exp2(x - lse2) = 0 there.
+template <int D>
+__global__ __launch_bounds__(256)
+void bwd_prep_kernel(BwdParams p) {
+  constexpr int KCH = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / KCH;
+  const int ch = (int)(gid % KCH);
+  if (row >= (int64_t)p.B * p.Lq_pad * p.Hq) return;   // whole KCH-lane groups exit together
+  const int h = (int)(row % p.Hq);
+  const int64_t bi = row / p.Hq;
+  const int i = (int)(bi % p.Lq_pad), b = (int)(bi / p.Lq_pad);
+  float s = 0.f;
+  if (i < p.Lq) {
+    const int64_t off = (int64_t)b * p.q_batch_stride + (int64_t)i * p.q_tok_stride + (int64_t)h * D + 8 * ch;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p.dout + off);
+    const u32x4 o = *reinterpret_cast<const u32x4*>(p.o + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += bf16lo(a[e]) * bf16lo(o[e]) + bf16hi(a[e]) * bf16hi(o[e]);
+  }
+#pragma unroll
+  for (int m = KCH / 2; m > 0; m >>= 1) s += __shfl_xor(s, m);
+  if (ch == 0) {
+    float l2 = INFINITY;
+    if (i < p.Lq) {
+      const float l = p.lse[((int64_t)b * p.Hq + h) * p.Lq + i];
+      l2 = l == -INFINITY ? INFINITY : l * kLog2eF;
+    }
+    const int64_t so = stat_offset(p, b, h, i);
+    p.stat[so] = l2;
+    p.stat[so + kBwdStatRows] = s;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPrefillThreads, 2)
+void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int KSTEPS = D / 16;                 // MFMA steps over d
+  constexpr int DBLK = D / 32;                   // 32-row blocks of dK^T, dV^T
+  constexpr int KCH = D / 8;                     // 16-byte chunks per row
+  constexpr int RPI = 64 / KCH;                  // rows per 1 KB load instruction
+  constexpr int LOADS = 64 / RPI / 4;            // load instructions per wave per tile
+  constexpr int TILE_BYTES = BLds<D>::kTile * 2;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2 * BLds<D>::kTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t do_lds[2 * BLds<D>::kTile];
+  __shared__ __attribute__((aligned(1024))) float st_lds[2 * 256];   // per buffer: lse2[64], delta[64]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hi = lane >> 5;
+  const int i16 = lane & 15, g16 = lane >> 4;
+
+  // ---- work item: (batch b, KV head g, key tile kt), early key tiles (which
+  // the most causal rows see) first; with the XCD-aware order all key tiles
+  // of a KV group run on one XCD, so its Q and dO stay in that L2.
+  int b, g, kt;
+  {
+    const int id = blockIdx.x;
+    if (p.xcd_groups > 0) {
+      const int x = id & 7, s = id >> 3;
+      const int grp = x + 8 * (s / p.num_k_tiles);
+      kt = s % p.num_k_tiles;
+      b = grp / p.Hkv;
+      g = grp - b * p.Hkv;
+    } else {
+      const int NG = p.B * p.Hkv;
+      kt = id / NG;
+      const int r = id - kt * NG;
+      b = r / p.Hkv;
+      g = r - b * p.Hkv;
+    }
+  }
+  const int Lq = p.Lq, Lk = p.Lk, delta = Lk - Lq;
+  const int k0 = kt * kBwdKeys;
+  const int kw0 = k0 + 32 * wave;
+  const int key = kw0 + n;
+  const int kend = min(k0 + kBwdKeys, Lk);
+
+  // ---- resident K^T and V^T (B operand): lane (key n, half hi) holds
+  // d = 16t + 8hi + 0..7 of its key; keys at or past Lk read zeros.
+  const int64_t kv_off = (int64_t)b * p.k_batch_stride + (int64_t)g * D;
+  u32x4 kf[KSTEPS], vf[KSTEPS];
+  {
+    const uint32_t kbytes = (uint32_t)(((int64_t)(Lk - 1) * p.k_tok_stride + D) * 2);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + kv_off, kbytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + kv_off, kbytes);
+    const uint32_t off = key < Lk ? (uint32_t)((int64_t)key * p.k_tok_stride + 8 * hi) * 2u : kOob;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      kf[t] = buf_load16(kr, off + 32u * t);
+      vf[t] = buf_load16(vr, off + 32u * t);
+    }
+  }
+
+  // ---- query rows that see any key of the workgroup -----------------------
+  // key_lo(i) and key_hi(i) grow with i: row i sees a key in [k0, kend) iff
+  // key_hi(i) > k0 and key_lo(i) < kend.
+  auto key_lo = [&](int row) { return p.win_left >= 0 ? max(0, row + delta - p.win_left) : 0; };
+  auto key_hi = [&](int row) {    // exclusive
+    int e = Lk;
+    if (p.causal) e = min(e, row + delta + 1);
+    if (p.win_right >= 0) e = min(e, row + delta + p.win_right + 1);
+    return e;
+  };
+  int64_t i_lo = 0, i_hi = Lq - 1;
+  if (p.causal) i_lo = max(i_lo, (int64_t)k0 - delta);
+  if (p.win_right >= 0) i_lo = max(i_lo, (int64_t)k0 - delta - p.win_right);
+  if (p.win_left >= 0) i_hi = min(i_hi, (int64_t)kend - 1 - delta + p.win_left);
+  const int qt_begin = (int)(i_lo / 64);
+  const int nq = i_hi >= i_lo ? (int)(i_hi / 64) - qt_begin + 1 : 0;
+  const int nsteps = p.group * nq;               // (query head, 64-row tile), head-major
+
+  // ---- staging: global -> LDS directly --------------------------------------
+  // Load instruction i of wave w fills tile bytes [(4i + w) KB, +1 KB): rows
+  // (4i + w) * RPI + lane / KCH, stored chunk lane % KCH holding logical chunk
+  // (lane % KCH) ^ swz(row); swz depends on row & 15, which i does not
+  // change, so each lane keeps one byte offset and the tile row goes in the
+  // scalar offset.  Rows at or past Lq fall outside the buffer and load as
+  // zeros.  Wave 0 also loads the tile's 64 lse2 and 64 delta values (512
+  // contiguous bytes of the statistics; lanes 32-63 load zeros).
+  const uint32_t q_row_bytes = (uint32_t)(p.q_tok_stride * 2);
+  const uint32_t q_bytes = (uint32_t)(((int64_t)(Lq - 1) * p.q_tok_stride + D) * 2);
+  uint32_t src;
+  {
+    const int r = wave * RPI + lane / KCH, slot = lane % KCH;
+    src = (uint32_t)r * q_row_bytes + (uint32_t)((slot ^ BLds<D>::swz(r)) * 16);
+  }
+  const uint32_t q_lds_addr = lds_address(q_lds), do_lds_addr = lds_address(do_lds);
+  const uint32_t st_lds_addr = lds_address(st_lds);
+  const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
+  const uint16_t* qb = p.q + (int64_t)b * p.q_batch_stride;
+  const uint16_t* dob = p.dout + (int64_t)b * p.q_batch_stride;
+  const uint32_t stat_bytes = (uint32_t)((int64_t)p.B * p.Hq * p.Lq_pad * 2 * 4);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.stat, stat_bytes);
+  const uint32_t st_src = lane < 32 ? 16u * lane : kOob;
+  auto fetch = [&](int s, int buf) {
+    const int hh = g * p.group + s / nq;
+    const int qt = qt_begin + s % nq;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb + (int64_t)hh * D, q_bytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dob + (int64_t)hh * D, q_bytes);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const uint32_t soff =
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(qt * 64 + 4 * i * RPI) * q_row_bytes));
+      lds_load16(qr, src, soff, q_lds_addr + buf * TILE_BYTES + wave_lds + 4096u * i);
+      lds_load16(dr, src, soff, do_lds_addr + buf * TILE_BYTES + wave_lds + 4096u * i);
+    }
+    if (wave == 0) {
+      const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)(stat_offset(p, b, hh, qt * 64) * 4));
+      lds_load16(srs, st_src, so, st_lds_addr + buf * 1024u);
+    }
+  };
+
+  // ---- LDS reads ----------------------------------------------------------
+  // Row reads (A operand of S = Q K^T and dP = dO V^T): lane (row n, half hi)
+  // reads logical chunk 2t + hi of row 32qh + n; the stored chunk's byte
+  // address is a per-lane base XOR 32t.
+  const uint32_t row_base = (uint32_t)(n * 2 * D) | ((16u * hi) ^ (16u * BLds<D>::swz(n)));
+  const char* q_lds_b = reinterpret_cast<const char*>(q_lds);
+  const char* do_lds_b = reinterpret_cast<const char*>(do_lds);
+  auto row_frag = [&](const char* tile, int qh, int t) {
+    return *reinterpret_cast<const u32x4*>(tile + 64 * qh * D + (row_base ^ (32u * t)));
+  };
+  // Transpose reads (A operand of dV^T = dO^T P and dK^T = Q^T dS): lane i of
+  // 16-lane group g addresses row 16cc + 8j + 4hi + i/4 and the 8-byte unit
+  // 8db + 4(g&1) + (i&3) of it, i.e. half i&1 of logical chunk
+  // 4db + 2(g&1) + (i&3)/2; the row's swizzle depends on j, hi and i/4, and
+  // db enters the stored chunk's byte address as XOR 64db.
+  uint32_t tr_base[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * j + 4 * hi + (i16 >> 2);
+    tr_base[j] = (uint32_t)(r * 2 * D) |
+                 ((((32u * (g16 & 1)) | (16u * ((i16 & 3) >> 1))) ^ (16u * BLds<D>::swz(r))) |
+                  (8u * (i16 & 1)));
+  }
+  auto tr_frag = [&](const char* tile, int cc, int db) {
+    const char* a = tile + 16 * cc * 2 * D;
+    const u32x2 lo = tr_read_b64(reinterpret_cast<const uint16_t*>(a + (tr_base[0] ^ (64u * db))));
+    const u32x2 hi2 = tr_read_b64(reinterpret_cast<const uint16_t*>(a + (tr_base[1] ^ (64u * db))));
+    return u32x4{lo[0], lo[1], hi2[0], hi2[1]};
+  };
+
+  f32x16 dka[DBLK], dva[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+  const float c = p.scale_log2;
+
+  // One step: the 64-row tile s (in buffer `cur`) against the wave's 32 keys.
+  auto step = [&](auto parity, int s) {
+    constexpr int cur = decltype(parity)::value;
+    if (s + 1 < nsteps) fetch(s + 1, cur ^ 1);
+    const int i0 = (qt_begin + s % nq) * 64;
+    // every (row, key) pair of the tile visible?  (rows past Lq have
+    // lse2 = +inf; keys past Lk only feed their own, unwritten, columns)
+    const int i_last = min(i0 + 63, Lq - 1);
+    const bool full = key_lo(i_last) <= kw0 && key_hi(i0) >= kw0 + 32;
+    const char* qt_b = q_lds_b + cur * TILE_BYTES;
+    const char* dt_b = do_lds_b + cur * TILE_BYTES;
+    const float* st = st_lds + cur * 256;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) {
+        S = mfma32x32x16(row_frag(qt_b, qh, t), kf[t], S);
+        dP = mfma32x32x16(row_frag(dt_b, qh, t), vf[t], dP);
+      }
+      // lane (key n, half hi) holds rows 32qh + 8j + 4hi + e of the tile in
+      // element 4j + e
+      u32x4 pf[2], dsf[2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + 32 * qh + 8 * j + 4 * hi);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(st + 64 + 32 * qh + 8 * j + 4 * hi);
+        float pv[4], dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pe = exp2_fast(fmaf(S[4 * j + e], c, -l2[e]));
+          if (!full) {
+            const int qi = i0 + 32 * qh + 8 * j + 4 * hi + e;
+            pe = (key >= key_lo(qi) && key < key_hi(qi)) ? pe : 0.f;
+          }
+          pv[e] = pe;
+          dv[e] = pe * (dP[4 * j + e] - dl[e]);
+        }
+        pf[j >> 1][2 * (j & 1)] = pack_bf16x2(pv[0], pv[1]);
+        pf[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(pv[2], pv[3]);
+        dsf[j >> 1][2 * (j & 1)] = pack_bf16x2(dv[0], dv[1]);
+        dsf[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(dv[2], dv[3]);
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          dva[db] = mfma32x32x16(tr_frag(dt_b, 2 * qh + c2, db), pf[c2], dva[db]);
+          dka[db] = mfma32x32x16(tr_frag(qt_b, 2 * qh + c2, db), dsf[c2], dka[db]);
+        }
+      }
+    }
+    lds_load_wait();
+    __syncthreads();
+  };
+
+  if (nsteps > 0) fetch(0, 0);
+  lds_load_wait();
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, s + 1);
+  }
+
+  // ---- epilogue: dK = scale * dK^T, dV = dV^T, rows of (b, key, g) --------
+  if (key < Lk) {
+    const int64_t ro = kv_off + (int64_t)key * p.k_tok_stride;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * db + 8 * gq + 4 * hi;
+        const f32x16& k_ = dka[db];
+        const f32x16& v_ = dva[db];
+        *reinterpret_cast<u32x2*>(p.dk + ro + d) =
+            u32x2{pack_bf16x2(k_[4 * gq] * p.scale, k_[4 * gq + 1] * p.scale),
+                  pack_bf16x2(k_[4 * gq + 2] * p.scale, k_[4 * gq + 3] * p.scale)};
+        *reinterpret_cast<u32x2*>(p.dv + ro + d) =
+            u32x2{pack_bf16x2(v_[4 * gq], v_[4 * gq + 1]), pack_bf16x2(v_[4 * gq + 2], v_[4 * gq + 3])};
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPrefillThreads, 2)
+void bwd_dq_kernel(BwdParams p) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr int KCH = D / 8;
+  constexpr int RPI = 64 / KCH;
+  constexpr int LOADS = kBlockN / RPI / 4;
+  constexpr int TILE_BYTES = BLds<D>::kTile * 2;
+
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * BLds<D>::kTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2 * BLds<D>::kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hi = lane >> 5;
+  const int i16 = lane & 15, g16 = lane >> 4;
+
+  const WorkItem w = map_work_dense(p, blockIdx.x);
+  const int Lq = p.Lq, Lk = p.Lk, delta = Lk - Lq;
+  const int kvh = w.h / p.group;
+  const int64_t q_off = (int64_t)w.b * p.q_batch_stride + (int64_t)w.h * D;
+  const int64_t kv_off = (int64_t)w.b * p.k_batch_stride + (int64_t)kvh * D;
+
+  // ---- key range of the workgroup and of this wave (as in the forward) ----
+  const int q0 = w.qt * kBlockM;
+  const int r_first = q0, r_last = min(q0 + kBlockM, Lq) - 1;
+  auto key_lo = [&](int row) { return p.win_left >= 0 ? max(0, row + delta - p.win_left) : 0; };
+  auto key_hi = [&](int row) {
+    int e = Lk;
+    if (p.causal) e = min(e, row + delta + 1);
+    if (p.win_right >= 0) e = min(e, row + delta + p.win_right + 1);
+    return e;
+  };
+  const int kv_lo = key_lo(r_first);
+  const int kv_hi = key_hi(r_last);
+  const int kt_begin = kv_lo / kBlockN;
+  const int kt_end = kv_hi > kv_lo ? (kv_hi + kBlockN - 1) / kBlockN : kt_begin;
+  const int ntiles = kt_end - kt_begin;
+  const int qw0 = q0 + 32 * wave;
+  const int rw0 = min(qw0, Lq - 1), rw1 = min(qw0 + 31, Lq - 1);
+  const int wlo_last = key_lo(rw1), whi_first = key_hi(rw0);
+  const int row = qw0 + n;
+  const int my_lo = key_lo(row), my_hi = key_hi(row);
+
+  // ---- resident Q^T and dO^T (B operand), the row's lse2 and delta --------
+  u32x4 qf[KSTEPS], dof[KSTEPS];
+  {
+    const uint32_t qbytes = (uint32_t)(((int64_t)(Lq - 1) * p.q_tok_stride + D) * 2);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + q_off, qbytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.dout + q_off, qbytes);
+    const uint32_t off = row < Lq ? (uint32_t)(row * p.q_tok_stride + 8 * hi) * 2u : kOob;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      qf[t] = buf_load16(qr, off + 32u * t);
+      dof[t] = buf_load16(dr, off + 32u * t);
+    }
+  }
+  const int64_t so = stat_offset(p, w.b, w.h, row);      // row < Lq_pad
+  const float lse2 = p.stat[so], dlt = p.stat[so + kBwdStatRows];
+
+  // ---- staging of K/V tiles (as in the forward, one swizzle for both) -----
+  const uint32_t k_row_bytes = (uint32_t)(p.k_tok_stride * 2);
+  const uint32_t k_bytes = (uint32_t)(((int64_t)(Lk - 1) * p.k_tok_stride + D) * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_off, k_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_off, k_bytes);
+  uint32_t src;
+  {
+    const int r = wave * RPI + lane / KCH, slot = lane % KCH;
+    src = (uint32_t)r * k_row_bytes + (uint32_t)((slot ^ BLds<D>::swz(r)) * 16);
+  }
+  const uint32_t k_lds_addr = lds_address(k_lds), v_lds_addr = lds_address(v_lds);
+  const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
+  auto fetch = [&](int kb, int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const uint32_t soff =
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(kb + 4 * i * RPI) * k_row_bytes));
+      lds_load16(krs, src, soff, k_lds_addr + buf * TILE_BYTES + wave_lds + 4096u * i);
+      lds_load16(vrs, src, soff, v_lds_addr + buf * TILE_BYTES + wave_lds + 4096u * i);
+    }
+  };
+
+  const uint32_t row_base = (uint32_t)(n * 2 * D) | ((16u * hi) ^ (16u * BLds<D>::swz(n)));
+  const char* k_lds_b = reinterpret_cast<const char*>(k_lds);
+  const char* v_lds_b = reinterpret_cast<const char*>(v_lds);
+  auto row_frag = [&](const char* tile, int kh, int t) {
+    return *reinterpret_cast<const u32x4*>(tile + 64 * kh * D + (row_base ^ (32u * t)));
+  };
+  uint32_t tr_base[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * j + 4 * hi + (i16 >> 2);
+    tr_base[j] = (uint32_t)(r * 2 * D) |
+                 ((((32u * (g16 & 1)) | (16u * ((i16 & 3) >> 1))) ^ (16u * BLds<D>::swz(r))) |
+                  (8u * (i16 & 1)));
+  }
+  auto tr_frag = [&](const char* tile, int cc, int db) {
+    const char* a = tile + 16 * cc * 2 * D;
+    const u32x2 lo = tr_read_b64(reinterpret_cast<const uint16_t*>(a + (tr_base[0] ^ (64u * db))));
+    const u32x2 hi2 = tr_read_b64(reinterpret_cast<const uint16_t*>(a + (tr_base[1] ^ (64u * db))));
+    return u32x4{lo[0], lo[1], hi2[0], hi2[1]};
+  };
+
+  f32x16 dqa[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) dqa[db] = f32x16{};
+  const float c = p.scale_log2;
+  const int kb0 = kt_begin * kBlockN;
+
+  auto step = [&](auto parity, int j) {
+    constexpr int cur = decltype(parity)::value;
+    const int kb = kb0 + j * kBlockN;
+    if (j + 1 < ntiles) fetch(kb + kBlockN, cur ^ 1);
+    const char* kt_b = k_lds_b + cur * TILE_BYTES;
+    const char* vt_b = v_lds_b + cur * TILE_BYTES;
+    const bool full = kb >= wlo_last && kb + kBlockN <= whi_first;
+    u32x4 dsf[4];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) {
+        S = mfma32x32x16(row_frag(kt_b, kh, t), qf[t], S);
+        dP = mfma32x32x16(row_frag(vt_b, kh, t), dof[t], dP);
+      }
+      // lane (row n, half hi) holds keys kb + 32kh + 8(r/4) + 4hi + r%4 in element r
+#pragma unroll
+      for (int r2 = 0; r2 < 8; ++r2) {
+        float ds[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 2 * r2 + u;
+          float pe = exp2_fast(fmaf(S[r], c, -lse2));
+          if (!full) {
+            const int kk = kb + 32 * kh + 8 * (r >> 2) + 4 * hi + (r & 3);
+            pe = (kk >= my_lo && kk < my_hi) ? pe : 0.f;
+          }
+          ds[u] = pe * (dP[r] - dlt);
+        }
+        dsf[2 * kh + (r2 >> 2)][r2 & 3] = pack_bf16x2(ds[0], ds[1]);
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) dqa[db] = mfma32x32x16(tr_frag(kt_b, cc, db), dsf[cc], dqa[db]);
+    }
+    lds_load_wait();
+    __syncthreads();
+  };
+
+  if (ntiles > 0) fetch(kb0, 0);
+  lds_load_wait();
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
+  }
+
+  // ---- epilogue: dQ = scale * dQ^T, row-major ------------------------------
+  if (row < Lq) {
+    uint16_t* drow = p.dq + q_off + (int64_t)row * p.q_tok_stride;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * db + 8 * gq + 4 * hi;
+        *reinterpret_cast<u32x2*>(drow + d) =
+            u32x2{pack_bf16x2(dqa[db][4 * gq] * p.scale, dqa[db][4 * gq + 1] * p.scale),
+                  pack_bf16x2(dqa[db][4 * gq + 2] * p.scale, dqa[db][4 * gq + 3] * p.scale)};
+      }
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  const int64_t prep_threads = (int64_t)p.B * p.Lq_pad * p.Hq * (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(p.B * p.Hkv * p.num_k_tiles)),
+                     dim3(kPrefillThreads), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(p.B * p.Hq * p.num_q_tiles)),
+                     dim3(kPrefillThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream) {
+  return d == 128 ? launch_bwd_d<128>(p, stream) : launch_bwd_d<64>(p, stream);
+}
+
+}  // namespace fa

@@ -390,4 +390,61 @@ fa_status fa_decode_paged_run(const void* q, const void* k_cache, const void* v_
                      window_left, split_tokens, workspace, workspace_bytes, stream);
 }
 
+size_t fa_bwd_workspace_size(int B, int Hq, int Lq) {
+  if (B < 1 || Hq < 1 || Lq < 1) return 0;
+  const int64_t lq_pad = cdiv(Lq, fa::kBlockM) * fa::kBlockM;
+  const int64_t bytes = (int64_t)B * Hq * lq_pad * 2 * (int64_t)sizeof(float);
+  if (bytes >= ((int64_t)1 << 31)) return 0;
+  return (size_t)bytes;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int Lq, int Lk, int Hq,
+                 int Hkv, int d, float softmax_scale, int causal, int window_left,
+                 int window_right, void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status st = check_common(Hq, Hkv, d, softmax_scale, causal, window_left, window_right);
+  if (st != FA_OK) return st;
+  if ((st = check_tensors(q, k, v, o, lse)) != FA_OK) return st;
+  if (!lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || Lq < 1 || Lk < 1) return FA_ERR_INVALID_ARG;
+  if ((int64_t)Lq * Hq * d >= kMaxBatchElems || (int64_t)Lk * Hkv * d >= kMaxBatchElems)
+    return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_workspace_size(B, Hq, Lq);
+  if (need == 0) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+
+  fa::BwdParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.stat = static_cast<float*>(workspace);
+  p.B = B; p.Lq = Lq; p.Lk = Lk;
+  p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.Lq_pad = (int)(cdiv(Lq, fa::kBlockM) * fa::kBlockM);
+  p.q_tok_stride = (int64_t)Hq * d;
+  p.k_tok_stride = (int64_t)Hkv * d;
+  p.q_batch_stride = (int64_t)Lq * Hq * d;
+  p.k_batch_stride = (int64_t)Lk * Hkv * d;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.scale = softmax_scale;
+  p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
+  p.num_k_tiles = (int)cdiv(Lk, fa::kBwdKeys);
+  p.xcd_groups = xcd_groups(B * Hkv);
+  p.chunk_groups = (int)std::max<int64_t>(1, fa::kPrefillSlotsPerXcd / ((int64_t)p.group * p.num_q_tiles));
+  if ((int64_t)p.num_q_tiles * B * Hq >= kMaxElems || (int64_t)p.num_k_tiles * B * Hkv >= kMaxElems)
+    return FA_ERR_INVALID_ARG;
+  if ((int64_t)B * p.Lq_pad * Hq * (d / 8) >= ((int64_t)1 << 40)) return FA_ERR_INVALID_ARG;
+  hipError_t e = fa::launch_bwd(p, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -65,6 +65,33 @@ struct AppendParams {
   int B, L_new, Hkv, d, page_size, max_blocks;
 };
 
+// Backward pass (dense layout).  Row statistics live in a caller workspace,
+// per (batch, query head) in blocks of 64 rows: [lse2 x 64][delta x 64] floats,
+// rows padded to a multiple of kBlockM (padded rows: lse2 = +inf, delta = 0).
+constexpr int kBwdStatRows = 64;
+struct BwdParams {
+  const uint16_t* q;       // (B, Lq, Hq, d) bf16 bits
+  const uint16_t* k;       // (B, Lk, Hkv, d)
+  const uint16_t* v;
+  const uint16_t* o;       // forward output (B, Lq, Hq, d)
+  const uint16_t* dout;    // upstream gradient (B, Lq, Hq, d)
+  const float* lse;        // forward LSE (B, Hq, Lq), natural log
+  uint16_t* dq;            // (B, Lq, Hq, d)
+  uint16_t* dk;            // (B, Lk, Hkv, d)
+  uint16_t* dv;
+  float* stat;             // workspace: lse2 = lse * log2(e) (+inf for rows with no key), delta = dO . O
+  int B, Lq, Lk, Hq, Hkv, group;
+  int Lq_pad;              // ceil(Lq / kBlockM) * kBlockM
+  int64_t q_tok_stride, k_tok_stride, q_batch_stride, k_batch_stride;
+  float scale_log2;        // softmax_scale * log2(e)
+  float scale;
+  int causal, win_left, win_right;
+  int num_q_tiles;         // ceil(Lq / kBlockM): dQ workgroups per (batch, head)
+  int num_k_tiles;         // ceil(Lk / kBwdKeys): dK/dV workgroups per (batch, KV head)
+  int xcd_groups, chunk_groups;
+};
+constexpr int kBwdKeys = 128;    // keys per dK/dV workgroup (4 waves x 32)
+
 struct DecodeParams {
   const uint16_t* q;
   const uint16_t* k_cache;
@@ -88,5 +115,7 @@ struct DecodeParams {
 hipError_t launch_prefill(const PrefillParams& p, int d, int mode, hipStream_t stream);
 hipError_t launch_append(const AppendParams& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, int rows, hipStream_t stream);
+// row statistics, then dK/dV, then dQ, in stream order
+hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
 
 }  // namespace fa

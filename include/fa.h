@@ -266,6 +266,35 @@ fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
                          float softcap, const float* alibi_slopes, int alibi_batch_stride,
                          void* stream);
 
+/*
+ * Backward pass of dense attention: dQ, dK, dV for an
+ * upstream gradient dO.  The score blocks are recomputed from the forward's
+ * LSE instead of being stored ("FlashAttention" concept page, recomputation;
+ * "FIA / FlashAttention" explainer, sec. 1); the values are the derivative of
+ * fa_fwd's definition:
+ *   P = exp(scale * Q K^T - LSE) (masked),  dV = P^T dO,
+ *   dS = P * (dO V^T - rowsum(dO * O)),  dQ = scale * dS K,  dK = scale * dS^T Q,
+ * with dK, dV of a KV head summed over its Hq / Hkv query heads (GQA).
+ *   q, o, dout, dq : (B, Lq, Hq, d) bf16     k, v, dk, dv : (B, Lk, Hkv, d) bf16
+ *   lse  : (B, Hq, Lq) float32, the LSE fa_fwd returned for these q, k, v and
+ *          mask (required); o: fa_fwd's output.
+ *   causal, window_left, window_right, softmax_scale: as given to fa_fwd.
+ *   workspace : device buffer of at least fa_bwd_workspace_size(B, Hq, Lq)
+ *       bytes, 256-byte aligned (per-row statistics); contents on entry do
+ *       not matter.
+ * Softcap and ALiBi are not supported here (forward only).  Every output
+ * element is summed in a fixed order by one wave, without atomics: results
+ * are bitwise identical from run to run (the deterministic mode of the
+ * skill page, sec. 3.3, is the only mode).  Keys no query row sees get
+ * dK = dV = 0; rows that see no key get dQ = 0.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Lq);
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int Lq, int Lk, int Hq,
+                 int Hkv, int d, float softmax_scale, int causal, int window_left,
+                 int window_right, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

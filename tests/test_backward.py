@@ -1,0 +1,91 @@
+"""GPU parity of the backward pass (fa_bwd, through the C ABI) against the CPU
+float64 oracle (oracle.attention_bwd_ref).
+
+The forward kernel produces O and LSE, fa_bwd the gradients; each element of
+dQ, dK, dV is compared with the oracle's gradient under the elementwise bound
+derived in tests/bwd_tolerance.py from the kernel's bf16 roundings.  Small
+cases span several 128-row / 128-key tiles with ragged tails and cover MHA,
+GQA, MQA, both head dims, Lq != Lk (rows that see no key, keys no row sees),
+causal, sliding and two-sided windows.  The causal MHA workload runs at full
+size with sampled rows and keys, and two runs must agree bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from bwd_tolerance import bwd_tolerance, key_rows_tolerance, query_rows_tolerance, ratio
+from gpu_helpers import bits, dev, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def make_case(seed, B, Lq, Lk, Hq, Hkv, d, causal, window):
+    w = workloads.random_dense(seed, B, Lq, Lk, Hq, Hkv, d, causal, window)
+    return w, workloads.upstream_grad(seed + 7919, (B, Lq, Hq, d))
+
+
+def run_bwd(fa, w, dout):
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    o, lse = fa.fa_fwd(q, k, v, w.scale, w.causal, w.window)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, lse, dev(dout), w.scale, w.causal, w.window)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+BWD_CASES = [
+    # B, Lq, Lk, Hq, Hkv, d, causal, window
+    (2, 200, 200, 4, 2, 128, True, (-1, -1)),
+    (1, 300, 300, 2, 1, 64, True, (50, 0)),
+    (2, 130, 257, 4, 4, 128, False, (-1, -1)),
+    (1, 257, 130, 3, 1, 64, True, (-1, -1)),       # Lq > Lk: the first 127 rows see nothing
+    (1, 64, 64, 8, 2, 128, False, (20, 20)),
+    (1, 1, 300, 2, 1, 128, True, (-1, -1)),       # one query row
+    (1, 513, 513, 2, 2, 128, True, (-1, -1)),
+    (1, 100, 400, 4, 1, 128, False, (30, 10)),    # keys no row sees
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c[:6])) + f"-c{int(c[6])}-w{c[7][0]}_{c[7][1]}")
+def test_bwd_sweep(fa, case):
+    w, dout = make_case(400 + sum(case[:6]), *case)
+    got = run_bwd(fa, w, dout)
+    qb, kb, vb, db = bits(w.q), bits(w.k), bits(w.v), bits(dout)
+    ref = oracle.attention_bwd_ref(qb, kb, vb, db, w.scale, w.causal, w.window)
+    tol = bwd_tolerance(qb, kb, vb, db, w.scale, w.causal, w.window, ref)
+    for name, g, r, t in zip(("dq", "dk", "dv"), got, ref, tol):
+        g = f64(g)
+        assert np.isfinite(g).all(), name
+        x = ratio(g, r, t)
+        print(f"[parity] bwd{case} {name}: max err/tol {x:.3f}", flush=True)
+        assert x <= 1.0, name
+
+
+def test_bwd_full_causal_mha_sampled_and_deterministic(fa):
+    w = workloads.causal_mha()
+    B, L, H, d = w.q.shape
+    dout = workloads.upstream_grad(1002, (B, L, H, d))
+    dq, dk, dv = run_bwd(fa, w, dout)
+    dq2, dk2, dv2 = run_bwd(fa, w, dout)
+    for a, b2 in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b2.view(torch.int16))     # bitwise reproducible
+    qb, kb, vb, db = bits(w.q), bits(w.k), bits(w.v), bits(dout)
+    rng = np.random.default_rng(12)
+    fixed = [0, 1, 63, 64, 127, 128, 1023, 2046, 2047]
+    for b, h in [(0, 0), (1, 17), (3, 31)]:
+        rows = np.unique(np.concatenate([fixed, rng.integers(0, L, 8)]))
+        ref = oracle.attention_bwd_query_rows_ref(qb, kb, vb, db, b, h, rows, w.scale, True)
+        tol = query_rows_tolerance(qb, kb, vb, db, b, h, rows, w.scale, True, (-1, -1), ref)
+        x = ratio(f64(dq[b, rows, h]), ref, tol)
+        print(f"[parity] bwd full dq b{b} h{h}: max err/tol {x:.3f}", flush=True)
+        assert x <= 1.0
+    for b, g in [(0, 5), (2, 30)]:
+        keys = np.unique(np.concatenate([fixed, rng.integers(0, L, 8)]))
+        rk, rv = oracle.attention_bwd_key_rows_ref(qb, kb, vb, db, b, g, keys, w.scale, True)
+        tk, tv = key_rows_tolerance(qb, kb, vb, db, b, g, keys, w.scale, True, (-1, -1), rk, rv)
+        xk = ratio(f64(dk[b, keys, g]), rk, tk)
+        xv = ratio(f64(dv[b, keys, g]), rv, tv)
+        print(f"[parity] bwd full dk/dv b{b} g{g}: max err/tol {xk:.3f} / {xv:.3f}", flush=True)
+        assert xk <= 1.0 and xv <= 1.0

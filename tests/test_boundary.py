@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["fa_status_string", "fa_fwd", "fa_fwd_varlen", "fa_varlen_plan",
                             "fa_fwd_varlen_run", "fa_decode_paged_workspace_size",
                             "fa_decode_paged", "fa_decode_plan", "fa_decode_paged_run",
-                            "fa_fwd_kvcache"])
+                            "fa_fwd_kvcache", "fa_bwd", "fa_bwd_workspace_size"])
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(fa.exported_symbols()) == names
@@ -251,3 +251,33 @@ def test_no_oracle_import_in_product():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt, f
+
+
+def bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=2, Lq=100, Lk=130, Hq=4, Hkv=2,
+             d=128, scale=0.1, causal=1, wl=-1, wr=-1, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                      a["B"], a["Lq"], a["Lk"], a["Hq"], a["Hkv"], a["d"], a["scale"], a["causal"],
+                      a["wl"], a["wr"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(do=None), INVALID),
+    (dict(dq=None), INVALID), (dict(dk=P + 8), INVALID), (dict(dv=P + 2), INVALID),
+    (dict(lse=P + 2), INVALID), (dict(B=0), INVALID), (dict(Lq=0), INVALID), (dict(Lk=0), INVALID),
+    (dict(Hq=5), INVALID), (dict(d=96), UNSUPPORTED), (dict(scale=float("nan")), INVALID),
+    (dict(causal=3), INVALID), (dict(wl=-2), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws=P + 64), WORKSPACE), (dict(wsb=1000), WORKSPACE),
+    (dict(B=1 << 14, Lq=1 << 15, Hq=4), INVALID),        # statistics beyond 2^31 bytes
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_bwd_workspace_size(lib):
+    # per (batch, head): rows padded to 128, two floats each
+    assert lib.fa_bwd_workspace_size(2, 4, 100) == 2 * 4 * 128 * 2 * 4
+    assert lib.fa_bwd_workspace_size(1, 1, 129) == 256 * 2 * 4
+    assert lib.fa_bwd_workspace_size(0, 4, 100) == 0
+    assert lib.fa_bwd_workspace_size(1 << 14, 4, 1 << 15) == 0

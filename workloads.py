@@ -203,6 +203,13 @@ def varlen_window(seed=5, nseq=16, H=16, d=64, lo=64, hi=8192, window=(4096, 0))
                   1.0 / math.sqrt(d))
 
 
+# ------------------------------------------------------- backward inputs
+def upstream_grad(seed, shape):
+    """Upstream gradient dO for the backward pass: N(0, 1) rounded to bf16
+    (same recipe as q, k, v), drawn from its own seed."""
+    return bf16_normal(np.random.default_rng(seed), shape)
+
+
 # ------------------------------------------------------------ small helpers
 def random_dense(seed, B, Lq, Lk, Hq, Hkv, d, causal=False, window=(-1, -1), scale=None):
     """Small dense case for parity sweeps (same recipe, arbitrary shape)."""
