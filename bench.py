@@ -174,6 +174,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time only the main workload")
     ap.add_argument("--only-decode", action="store_true", help="time only the paged decode workload")
+    ap.add_argument("--only-bwd", action="store_true", help="time only the backward workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain copy of known size (for byte-counter scaling)")
     args = ap.parse_args()
@@ -196,14 +197,16 @@ def main():
               "data": "synthetic", "device": props.name, "prewarm_ms": args.prewarm_ms}
     w2 = workloads.causal_mha()
     flops2 = dense_flops(w2)
-    if not args.only_decode:
+    if not args.only_decode and not args.only_bwd:
         result.update(bench_main(fa, w2, flops2, args))
     wl = {}
-    if not args.only_main:
+    if args.only_bwd:
+        wl = bench_bwd(fa, args)
+    elif not args.only_main:
         wl, roof_dec = bench_others(fa, args)
         result["roofline_decode"] = roof_dec
     result["workloads"] = wl
-    if not args.no_cpu_baseline and not args.only_decode:
+    if not args.no_cpu_baseline and not args.only_decode and not args.only_bwd:
         result["cpu_baseline"] = cpu_baseline(w2, flops2)
     print(json.dumps(result), flush=True)
 
@@ -238,6 +241,28 @@ def bench_main(fa, w2, flops2, args):
     }
 
 
+def bench_bwd(fa, args):
+    """Backward of the causal MHA workload: prep + dK/dV + dQ kernels; algorithmic
+    work = the five products of the chain rule (S, dP, dV, dK, dQ), 2.5x the forward."""
+    wl = {}
+    w2 = workloads.causal_mha()
+    a = [t.cuda() for t in (w2.q, w2.k, w2.v)]
+    do2 = workloads.upstream_grad(1002, tuple(w2.q.shape)).cuda()
+    o2, l2 = fa.fa_fwd(*a, w2.scale, True)
+    gq, gk, gv = torch.empty_like(a[0]), torch.empty_like(a[1]), torch.empty_like(a[2])
+    ws2 = torch.empty(fa.fa_bwd_workspace_size(4, 32, 2048), dtype=torch.uint8, device="cuda")
+    fb = 2.5 * dense_flops(w2)
+    ms = time_calls(lambda: fa.fa_bwd(*a, o2, l2, do2, w2.scale, True, dq=gq, dk=gk, dv=gv,
+                                      workspace=ws2), max(20, args.steps // 4), args.warmup,
+                    args.prewarm_ms)
+    wl["bwd_causal_mha"] = {"ms": round(ms, 4), "TFLOP/s": round(fb / ms / 1e9, 2),
+                            "frac_mfma": round(fb / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": fb,
+                            "kernels": "bwd_prep + bwd_dkdv + bwd_dq"}
+    del a, do2, o2, l2, gq, gk, gv, ws2, w2
+    torch.cuda.empty_cache()
+    return wl
+
+
 def bench_others(fa, args):
     """Time the remaining workloads; returns (per-workload dict, decode roofline)."""
     wl = {}
@@ -247,6 +272,8 @@ def bench_others(fa, args):
         ms = time_calls(lambda: fa.fa_fwd(*a, w1.scale, False), args.steps, args.warmup, args.prewarm_ms)
         wl["small_dense"] = {"ms": round(ms, 4), "TFLOP/s": round(dense_flops(w1) / ms / 1e9, 3)}
         del a
+
+        wl.update(bench_bwd(fa, args))
 
         w3 = workloads.causal_gqa_long()
         a = [t.cuda() for t in (w3.q, w3.k, w3.v)]

@@ -14,15 +14,16 @@
 // Mapping onto CDNA4 (our design, not the pages'):
 //   * bwd_prep_kernel: delta = dO . O and lse2 = LSE * log2(e) per query row,
 //     one coalesced pass over dO and O, into a caller workspace.
-//   * bwd_dkdv_kernel: a workgroup owns 128 keys of one (batch, KV head), 32
-//     per wave.  The wave's K and V rows stay in registers as MFMA B
-//     operands; its dK^T and dV^T accumulate in registers over every query
-//     row of every query head of the group, streamed through LDS in 64-row
-//     tiles.  Per 32-row half, S = Q K^T and dP = dO V^T take Q and dO rows
-//     from LDS as the A operand; the accumulator gives each lane one key and
-//     16 query rows, which rounded to bf16 are exactly the B operand of
-//     dV^T += dO^T P and dK^T += Q^T dS (A = dO^T and Q^T by transpose reads),
-//     so P and dS never leave registers.
+//   * bwd_dkdv_kernel: a workgroup owns 128 keys of one (batch, KV head) and
+//     has 8 waves, two per 32-key block: one keeps K resident (MFMA B
+//     operand) and accumulates dV^T, its partner keeps V resident and
+//     accumulates dK^T, over every query row of every query head of the
+//     group, streamed through LDS in 64-row tiles.  Per 32-row half,
+//     S = Q K^T and dP = dO V^T take Q and dO rows from LDS as the A operand;
+//     the accumulator gives each lane one key and 16 query rows, which
+//     rounded to bf16 are exactly the B operand of dV^T += dO^T P and
+//     dK^T += Q^T dS (A = dO^T and Q^T by transpose reads).  P goes to the
+//     partner through LDS (fp32).
 //   * bwd_dq_kernel: a workgroup owns 128 query rows of one (batch, head), 32
 //     per wave, as in the forward; the wave's Q and dO rows stay in registers
 //     as B operands while K and V stream through LDS in 64-key tiles:
@@ -76,7 +77,8 @@ FA_DEV int64_t stat_offset(const BwdParams& p, int b, int h, int i) {
 
 }  // namespace
 
-// One group of D/8 lanes per (batch, row, head), rows padded to Lq_pad:
+// One group of D/8 lanes per (batch, head, row), rows padded to Lq_pad, so
+// consecutive groups write consecutive statistics:
 // delta = sum_d dO * O in fp32 (fixed order), lse2 = LSE * log2(e), or +inf
 // for a row with no visible key (LSE = -inf) and for padding rows, so that
 // exp2(x - lse2) = 0 there.
@@ -88,9 +90,9 @@ void bwd_prep_kernel(BwdParams p) {
   const int64_t row = gid / KCH;
   const int ch = (int)(gid % KCH);
   if (row >= (int64_t)p.B * p.Lq_pad * p.Hq) return;   // whole KCH-lane groups exit together
-  const int h = (int)(row % p.Hq);
-  const int64_t bi = row / p.Hq;
-  const int i = (int)(bi % p.Lq_pad), b = (int)(bi / p.Lq_pad);
+  const int i = (int)(row % p.Lq_pad);
+  const int64_t bh = row / p.Lq_pad;
+  const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
   float s = 0.f;
   if (i < p.Lq) {
     const int64_t off = (int64_t)b * p.q_batch_stride + (int64_t)i * p.q_tok_stride + (int64_t)h * D + 8 * ch;
@@ -113,22 +115,34 @@ void bwd_prep_kernel(BwdParams p) {
   }
 }
 
+// Split roles: 8 waves, two per 32-key block.  Wave w < 4 (the "P" wave)
+// keeps K^T of keys 32w.. resident, computes S and P and accumulates dV^T;
+// wave w + 4 (the "dS" wave, on the same SIMD) keeps V^T resident, computes
+// dP, takes P (fp32) from its partner through LDS, forms dS and accumulates
+// dK^T.  Each wave then holds one resident operand and one accumulator, and
+// the MFMA work of a block splits evenly between the pair.
+constexpr int kDkdvThreads = 512;
+
 template <int D>
-__global__ __launch_bounds__(kPrefillThreads, 2)
+__global__ __launch_bounds__(kDkdvThreads, 1)
 void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KSTEPS = D / 16;                 // MFMA steps over d
   constexpr int DBLK = D / 32;                   // 32-row blocks of dK^T, dV^T
   constexpr int KCH = D / 8;                     // 16-byte chunks per row
   constexpr int RPI = 64 / KCH;                  // rows per 1 KB load instruction
-  constexpr int LOADS = 64 / RPI / 4;            // load instructions per wave per tile
   constexpr int TILE_BYTES = BLds<D>::kTile * 2;
+  constexpr int LOADS = TILE_BYTES / 1024 / 8;   // load instructions per wave per tile
+  static_assert(LOADS >= 1, "tile smaller than one load per wave");
 
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2 * BLds<D>::kTile];
   __shared__ __attribute__((aligned(1024))) uint16_t do_lds[2 * BLds<D>::kTile];
   __shared__ __attribute__((aligned(1024))) float st_lds[2 * 256];   // per buffer: lse2[64], delta[64]
+  // P of a 32-row half, per key block: [half][block][j][lane][4] floats
+  __shared__ __attribute__((aligned(16))) float x_lds[2][4][4][64][4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int blk = wave & 3, role = wave >> 2;    // role 0: S, P, dV; role 1: dP, dS, dK
   const int n = lane & 31, hi = lane >> 5;
   const int i16 = lane & 15, g16 = lane >> 4;
 
@@ -154,24 +168,20 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   const int Lq = p.Lq, Lk = p.Lk, delta = Lk - Lq;
   const int k0 = kt * kBwdKeys;
-  const int kw0 = k0 + 32 * wave;
+  const int kw0 = k0 + 32 * blk;
   const int key = kw0 + n;
   const int kend = min(k0 + kBwdKeys, Lk);
 
-  // ---- resident K^T and V^T (B operand): lane (key n, half hi) holds
-  // d = 16t + 8hi + 0..7 of its key; keys at or past Lk read zeros.
+  // ---- resident operand (B): K^T (role 0) or V^T (role 1); lane (key n,
+  // half hi) holds d = 16t + 8hi + 0..7 of its key; keys past Lk read zeros.
   const int64_t kv_off = (int64_t)b * p.k_batch_stride + (int64_t)g * D;
-  u32x4 kf[KSTEPS], vf[KSTEPS];
+  u32x4 rf[KSTEPS];
   {
     const uint32_t kbytes = (uint32_t)(((int64_t)(Lk - 1) * p.k_tok_stride + D) * 2);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + kv_off, kbytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + kv_off, kbytes);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc((role == 0 ? p.k : p.v) + kv_off, kbytes);
     const uint32_t off = key < Lk ? (uint32_t)((int64_t)key * p.k_tok_stride + 8 * hi) * 2u : kOob;
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-      kf[t] = buf_load16(kr, off + 32u * t);
-      vf[t] = buf_load16(vr, off + 32u * t);
-    }
+    for (int t = 0; t < KSTEPS; ++t) rf[t] = buf_load16(rr, off + 32u * t);
   }
 
   // ---- query rows that see any key of the workgroup -----------------------
@@ -188,13 +198,21 @@ void bwd_dkdv_kernel(BwdParams p) {
   if (p.causal) i_lo = max(i_lo, (int64_t)k0 - delta);
   if (p.win_right >= 0) i_lo = max(i_lo, (int64_t)k0 - delta - p.win_right);
   if (p.win_left >= 0) i_hi = min(i_hi, (int64_t)kend - 1 - delta + p.win_left);
+  // Rows that see this lane's key: qmin <= i <= qmax (the key is visible to
+  // row i iff key_lo(i) <= key < key_hi(i)); keys past Lk only feed their
+  // own, unwritten, columns.
+  int64_t qmin = -((int64_t)1 << 40), qmax = (int64_t)1 << 40;
+  if (p.causal) qmin = max(qmin, (int64_t)key - delta);
+  if (p.win_right >= 0) qmin = max(qmin, (int64_t)key - delta - p.win_right);
+  if (p.win_left >= 0) qmax = (int64_t)key - delta + p.win_left;
+  const int qmin_c = (int)max(qmin, (int64_t)-1), qmax_c = (int)min(qmax, (int64_t)Lq);
   const int qt_begin = (int)(i_lo / 64);
   const int nq = i_hi >= i_lo ? (int)(i_hi / 64) - qt_begin + 1 : 0;
   const int nsteps = p.group * nq;               // (query head, 64-row tile), head-major
 
   // ---- staging: global -> LDS directly --------------------------------------
-  // Load instruction i of wave w fills tile bytes [(4i + w) KB, +1 KB): rows
-  // (4i + w) * RPI + lane / KCH, stored chunk lane % KCH holding logical chunk
+  // Load instruction i of wave w fills tile bytes [(8i + w) KB, +1 KB): rows
+  // (8i + w) * RPI + lane / KCH, stored chunk lane % KCH holding logical chunk
   // (lane % KCH) ^ swz(row); swz depends on row & 15, which i does not
   // change, so each lane keeps one byte offset and the tile row goes in the
   // scalar offset.  Rows at or past Lq fall outside the buffer and load as
@@ -223,9 +241,9 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const uint32_t soff =
-          (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(qt * 64 + 4 * i * RPI) * q_row_bytes));
-      lds_load16(qr, src, soff, q_lds_addr + buf * TILE_BYTES + wave_lds + 4096u * i);
-      lds_load16(dr, src, soff, do_lds_addr + buf * TILE_BYTES + wave_lds + 4096u * i);
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(qt * 64 + 8 * i * RPI) * q_row_bytes));
+      lds_load16(qr, src, soff, q_lds_addr + buf * TILE_BYTES + wave_lds + 8192u * i);
+      lds_load16(dr, src, soff, do_lds_addr + buf * TILE_BYTES + wave_lds + 8192u * i);
     }
     if (wave == 0) {
       const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)(stat_offset(p, b, hh, qt * 64) * 4));
@@ -238,8 +256,6 @@ void bwd_dkdv_kernel(BwdParams p) {
   // reads logical chunk 2t + hi of row 32qh + n; the stored chunk's byte
   // address is a per-lane base XOR 32t.
   const uint32_t row_base = (uint32_t)(n * 2 * D) | ((16u * hi) ^ (16u * BLds<D>::swz(n)));
-  const char* q_lds_b = reinterpret_cast<const char*>(q_lds);
-  const char* do_lds_b = reinterpret_cast<const char*>(do_lds);
   auto row_frag = [&](const char* tile, int qh, int t) {
     return *reinterpret_cast<const u32x4*>(tile + 64 * qh * D + (row_base ^ (32u * t)));
   };
@@ -262,65 +278,79 @@ void bwd_dkdv_kernel(BwdParams p) {
     const u32x2 hi2 = tr_read_b64(reinterpret_cast<const uint16_t*>(a + (tr_base[1] ^ (64u * db))));
     return u32x4{lo[0], lo[1], hi2[0], hi2[1]};
   };
+  // the role's row operand (Q for S, dO for dP) and transposed operand (dO^T
+  // for dV, Q^T for dK)
+  const char* row_tiles = reinterpret_cast<const char*>(role == 0 ? q_lds : do_lds);
+  const char* tr_tiles = reinterpret_cast<const char*>(role == 0 ? do_lds : q_lds);
 
-  f32x16 dka[DBLK], dva[DBLK];
+  f32x16 acc[DBLK];
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db) {
-    dka[db] = f32x16{};
-    dva[db] = f32x16{};
-  }
+  for (int db = 0; db < DBLK; ++db) acc[db] = f32x16{};
   const float c = p.scale_log2;
 
-  // One step: the 64-row tile s (in buffer `cur`) against the wave's 32 keys.
+  // One step: the 64-row tile s (in buffer `cur`) against the pair's 32 keys,
+  // as two 32-row halves.  Lane (key n, half hi) holds rows 32qh + 8j + 4hi + e
+  // of the tile in element 4j + e of S and dP.
   auto step = [&](auto parity, int s) {
     constexpr int cur = decltype(parity)::value;
     if (s + 1 < nsteps) fetch(s + 1, cur ^ 1);
     const int i0 = (qt_begin + s % nq) * 64;
-    // every (row, key) pair of the tile visible?  (rows past Lq have
-    // lse2 = +inf; keys past Lk only feed their own, unwritten, columns)
     const int i_last = min(i0 + 63, Lq - 1);
     const bool full = key_lo(i_last) <= kw0 && key_hi(i0) >= kw0 + 32;
-    const char* qt_b = q_lds_b + cur * TILE_BYTES;
-    const char* dt_b = do_lds_b + cur * TILE_BYTES;
+    // offsets within the tile (from row i0 + 4hi) of the lane's visible rows:
+    // rlo .. rlo + rcount - 1 (rcount = 0 when no row sees the key)
+    const int rlo = qmin_c - i0 - 4 * hi;
+    const uint32_t rcount = (uint32_t)max(qmax_c - qmin_c + 1, 0);
+    const char* rt = row_tiles + cur * TILE_BYTES;
+    const char* tt = tr_tiles + cur * TILE_BYTES;
     const float* st = st_lds + cur * 256;
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
-      f32x16 S = f32x16{}, dP = f32x16{};
+      f32x16 S = f32x16{};
 #pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-        S = mfma32x32x16(row_frag(qt_b, qh, t), kf[t], S);
-        dP = mfma32x32x16(row_frag(dt_b, qh, t), vf[t], dP);
-      }
-      // lane (key n, half hi) holds rows 32qh + 8j + 4hi + e of the tile in
-      // element 4j + e
-      u32x4 pf[2], dsf[2];
+      for (int t = 0; t < KSTEPS; ++t) S = mfma32x32x16(row_frag(rt, qh, t), rf[t], S);
+      float (*xs)[64][4] = x_lds[qh][blk];
+      u32x4 ops[2];
+      if (role == 0) {
+        // P = 2^(S c - lse2), masked; to the partner as fp32, to dV as bf16
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + 32 * qh + 8 * j + 4 * hi);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(st + 64 + 32 * qh + 8 * j + 4 * hi);
-        float pv[4], dv[4];
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + 32 * qh + 8 * j + 4 * hi);
+          f32x4 pv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pe = exp2_fast(fmaf(S[4 * j + e], c, -l2[e]));
-          if (!full) {
-            const int qi = i0 + 32 * qh + 8 * j + 4 * hi + e;
-            pe = (key >= key_lo(qi) && key < key_hi(qi)) ? pe : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            float pe = exp2_fast(fmaf(S[4 * j + e], c, -l2[e]));
+            if (!full) {
+              const uint32_t off = (uint32_t)(32 * qh + 8 * j + e);
+              pe = (off - (uint32_t)rlo) < rcount ? pe : 0.f;
+            }
+            pv[e] = pe;
           }
-          pv[e] = pe;
-          dv[e] = pe * (dP[4 * j + e] - dl[e]);
+          *reinterpret_cast<f32x4*>(xs[j][lane]) = pv;
+          ops[j >> 1][2 * (j & 1)] = pack_bf16x2(pv[0], pv[1]);
+          ops[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(pv[2], pv[3]);
         }
-        pf[j >> 1][2 * (j & 1)] = pack_bf16x2(pv[0], pv[1]);
-        pf[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(pv[2], pv[3]);
-        dsf[j >> 1][2 * (j & 1)] = pack_bf16x2(dv[0], dv[1]);
-        dsf[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(dv[2], dv[3]);
       }
+      __syncthreads();   // P of this half is in x_lds
+      if (role == 1) {
+        // dS = P (dP - delta), S holding dP here
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 dl = *reinterpret_cast<const f32x4*>(st + 64 + 32 * qh + 8 * j + 4 * hi);
+          const f32x4 pv = *reinterpret_cast<const f32x4*>(xs[j][lane]);
+          float dv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dv[e] = pv[e] * (S[4 * j + e] - dl[e]);
+          ops[j >> 1][2 * (j & 1)] = pack_bf16x2(dv[0], dv[1]);
+          ops[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(dv[2], dv[3]);
+        }
+      }
+      // role 0: dV^T += dO^T P; role 1: dK^T += Q^T dS
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          dva[db] = mfma32x32x16(tr_frag(dt_b, 2 * qh + c2, db), pf[c2], dva[db]);
-          dka[db] = mfma32x32x16(tr_frag(qt_b, 2 * qh + c2, db), dsf[c2], dka[db]);
-        }
+        for (int db = 0; db < DBLK; ++db)
+          acc[db] = mfma32x32x16(tr_frag(tt, 2 * qh + c2, db), ops[c2], acc[db]);
       }
     }
     lds_load_wait();
@@ -335,21 +365,18 @@ void bwd_dkdv_kernel(BwdParams p) {
     if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, s + 1);
   }
 
-  // ---- epilogue: dK = scale * dK^T, dV = dV^T, rows of (b, key, g) --------
+  // ---- epilogue: role 0 writes dV = dV^T, role 1 dK = scale * dK^T --------
   if (key < Lk) {
-    const int64_t ro = kv_off + (int64_t)key * p.k_tok_stride;
+    uint16_t* dst = (role == 0 ? p.dv : p.dk) + kv_off + (int64_t)key * p.k_tok_stride;
+    const float f = role == 0 ? 1.f : p.scale;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int d = 32 * db + 8 * gq + 4 * hi;
-        const f32x16& k_ = dka[db];
-        const f32x16& v_ = dva[db];
-        *reinterpret_cast<u32x2*>(p.dk + ro + d) =
-            u32x2{pack_bf16x2(k_[4 * gq] * p.scale, k_[4 * gq + 1] * p.scale),
-                  pack_bf16x2(k_[4 * gq + 2] * p.scale, k_[4 * gq + 3] * p.scale)};
-        *reinterpret_cast<u32x2*>(p.dv + ro + d) =
-            u32x2{pack_bf16x2(v_[4 * gq], v_[4 * gq + 1]), pack_bf16x2(v_[4 * gq + 2], v_[4 * gq + 3])};
+        *reinterpret_cast<u32x2*>(dst + d) =
+            u32x2{pack_bf16x2(acc[db][4 * gq] * f, acc[db][4 * gq + 1] * f),
+                  pack_bf16x2(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
       }
     }
   }
@@ -472,6 +499,7 @@ void bwd_dq_kernel(BwdParams p) {
     const char* kt_b = k_lds_b + cur * TILE_BYTES;
     const char* vt_b = v_lds_b + cur * TILE_BYTES;
     const bool full = kb >= wlo_last && kb + kBlockN <= whi_first;
+    const int klo = my_lo - kb - 4 * hi, kspan = max(my_hi - my_lo, 0);
     u32x4 dsf[4];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -490,8 +518,9 @@ void bwd_dq_kernel(BwdParams p) {
           const int r = 2 * r2 + u;
           float pe = exp2_fast(fmaf(S[r], c, -lse2));
           if (!full) {
-            const int kk = kb + 32 * kh + 8 * (r >> 2) + 4 * hi + (r & 3);
-            pe = (kk >= my_lo && kk < my_hi) ? pe : 0.f;
+            // key kb + 4hi + off visible iff my_lo <= key < my_hi
+            const uint32_t off = (uint32_t)(32 * kh + 8 * (r >> 2) + (r & 3));
+            pe = (off - (uint32_t)klo) < (uint32_t)kspan ? pe : 0.f;
           }
           ds[u] = pe * (dP[r] - dlt);
         }
@@ -539,7 +568,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(p.B * p.Hkv * p.num_k_tiles)),
-                     dim3(kPrefillThreads), 0, stream, p);
+                     dim3(kDkdvThreads), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(p.B * p.Hq * p.num_q_tiles)),
                      dim3(kPrefillThreads), 0, stream, p);
