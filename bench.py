@@ -260,6 +260,23 @@ def bench_bwd(fa, args):
                             "kernels": "bwd_prep + bwd_dkdv + bwd_dq"}
     del a, do2, o2, l2, gq, gk, gv, ws2, w2
     torch.cuda.empty_cache()
+    if not args.only_bwd:
+        # long-context GQA backward (B=1, Hq=32, Hkv=8, L=16384): dK, dV of a KV
+        # head sum its 4 query heads inside one workgroup
+        w3 = workloads.causal_gqa_long()
+        a = [t.cuda() for t in (w3.q, w3.k, w3.v)]
+        do3 = workloads.upstream_grad(1003, tuple(w3.q.shape)).cuda()
+        o3, l3 = fa.fa_fwd(*a, w3.scale, True)
+        ws3 = torch.empty(fa.fa_bwd_workspace_size(1, 32, 16384), dtype=torch.uint8, device="cuda")
+        g3 = [torch.empty_like(t) for t in a]
+        fb3 = 2.5 * dense_flops(w3)
+        ms = time_calls(lambda: fa.fa_bwd(*a, o3, l3, do3, w3.scale, True, dq=g3[0], dk=g3[1],
+                                          dv=g3[2], workspace=ws3), 5, 2, args.prewarm_ms)
+        wl["bwd_causal_gqa_long"] = {"ms": round(ms, 4), "TFLOP/s": round(fb3 / ms / 1e9, 2),
+                                     "frac_mfma": round(fb3 / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                     "flops": fb3}
+        del a, do3, o3, l3, ws3, g3, w3
+        torch.cuda.empty_cache()
     return wl
 
 

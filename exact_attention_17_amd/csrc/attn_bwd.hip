@@ -86,13 +86,14 @@ template <int D>
 __global__ __launch_bounds__(256)
 void bwd_prep_kernel(BwdParams p) {
   constexpr int KCH = D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / KCH;
+  // B * Hq * Lq_pad < 2^28 (the statistics are < 2^31 bytes): 32-bit indices
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t row = gid / KCH;
   const int ch = (int)(gid % KCH);
-  if (row >= (int64_t)p.B * p.Lq_pad * p.Hq) return;   // whole KCH-lane groups exit together
-  const int i = (int)(row % p.Lq_pad);
-  const int64_t bh = row / p.Lq_pad;
-  const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+  if (row >= (uint32_t)(p.B * p.Hq * p.Lq_pad)) return;   // whole KCH-lane groups exit together
+  const uint32_t bh = row / (uint32_t)p.Lq_pad;
+  const int i = (int)(row - bh * (uint32_t)p.Lq_pad);
+  const int b = (int)(bh / (uint32_t)p.Hq), h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
   float s = 0.f;
   if (i < p.Lq) {
     const int64_t off = (int64_t)b * p.q_batch_stride + (int64_t)i * p.q_tok_stride + (int64_t)h * D + 8 * ch;
