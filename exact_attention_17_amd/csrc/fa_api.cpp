@@ -50,6 +50,11 @@ void set_mods(fa::PrefillParams& p, float scale, float softcap, const float* ali
   p.alibi_scale = 1.f / scale;
 }
 
+// A window side of 2^30 or more reaches past every key (sequence lengths are
+// below 2^24 at d >= 64), so it is the same as an unbounded side; normalising
+// it keeps the kernels' 32-bit position sums (row + offset + window) in range.
+int norm_window(int w) { return w >= (1 << 30) ? -1 : w; }
+
 // XCD-aware mapping needs the KV-group count to split evenly over 8 XCDs.
 int xcd_groups(int kv_groups) { return (kv_groups > 0 && kv_groups % 8 == 0) ? kv_groups : 0; }
 
@@ -104,7 +109,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.k_batch_stride = (int64_t)Lk * Hkv * d;
   p.lse_seq_stride = Lq;
   p.scale_log2 = softmax_scale * kLog2e;
-  p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  p.causal = causal; p.win_left = norm_window(window_left); p.win_right = norm_window(window_right);
   set_mods(p, softmax_scale, softcap, alibi_slopes, alibi_batch_stride);
   p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
   p.xcd_groups = xcd_groups(B * Hkv);
@@ -155,7 +160,7 @@ fa_status varlen_impl(const void* q, const void* k, const void* v, void* o, floa
   p.k_tok_stride = (int64_t)Hkv * d;
   p.lse_seq_stride = total_q;
   p.scale_log2 = softmax_scale * kLog2e;
-  p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  p.causal = causal; p.win_left = norm_window(window_left); p.win_right = norm_window(window_right);
   set_mods(p, softmax_scale, softcap, alibi_slopes, alibi_batch_stride);
   if (plan) {
     p.plan = plan;
@@ -259,7 +264,7 @@ fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
   p.k_batch_stride = 0;
   p.lse_seq_stride = Lq;
   p.scale_log2 = softmax_scale * kLog2e;
-  p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  p.causal = causal; p.win_left = norm_window(window_left); p.win_right = norm_window(window_right);
   set_mods(p, softmax_scale, softcap, alibi_slopes, alibi_batch_stride);
   p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
   p.xcd_groups = xcd_groups(B * Hkv);
@@ -356,7 +361,7 @@ fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   p.part_o = static_cast<float*>(workspace);
   p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_o_bytes(B, Hq, d, p.max_splits));
   p.scale_log2 = softmax_scale * kLog2e;
-  p.win_left = window_left;
+  p.win_left = norm_window(window_left);
   p.planned = planned;
   p.plan = plan;
   p.num_items = num_items;
@@ -435,7 +440,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   p.k_batch_stride = (int64_t)Lk * Hkv * d;
   p.scale_log2 = softmax_scale * kLog2e;
   p.scale = softmax_scale;
-  p.causal = causal; p.win_left = window_left; p.win_right = window_right;
+  p.causal = causal; p.win_left = norm_window(window_left); p.win_right = norm_window(window_right);
   p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
   p.num_k_tiles = (int)cdiv(Lk, fa::kBwdKeys);
   p.xcd_groups = xcd_groups(B * Hkv);

@@ -89,3 +89,14 @@ def test_bwd_full_causal_mha_sampled_and_deterministic(fa):
         xv = ratio(f64(dv[b, keys, g]), rv, tv)
         print(f"[parity] bwd full dk/dv b{b} g{g}: max err/tol {xk:.3f} / {xv:.3f}", flush=True)
         assert xk <= 1.0 and xv <= 1.0
+
+
+def test_bwd_huge_window_equals_unbounded(fa):
+    w, dout = make_case(77, 1, 150, 200, 4, 2, 128, True, (-1, -1))
+    q, k, v, do = dev(w.q), dev(w.k), dev(w.v), dev(dout)
+    o, lse = fa.fa_fwd(q, k, v, w.scale, True)
+    a = fa.fa_bwd(q, k, v, o, lse, do, w.scale, True, (2 ** 31 - 1, 2 ** 31 - 1))
+    b = fa.fa_bwd(q, k, v, o, lse, do, w.scale, True, (-1, -1))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))

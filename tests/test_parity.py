@@ -85,6 +85,30 @@ def test_dense_large_scale_values(fa):
     check("large_scale", o, lse, O, LSE)
 
 
+def test_huge_windows_equal_unbounded(fa):
+    """A window side of 2^31 - 1 reaches every key: results must equal the
+    unbounded side bit for bit (regression: the kernels' row + window sums
+    must not overflow)."""
+    big = 2 ** 31 - 1
+    w = workloads.random_dense(79, 2, 200, 300, 4, 2, 128, False)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    for causal, win, ref_win in [(False, (big, big), (-1, -1)), (True, (big, -1), (-1, -1)),
+                                 (False, (big, 5), (-1, 5)), (False, (7, big), (7, -1))]:
+        o1, l1 = fa.fa_fwd(q, k, v, w.scale, causal, win)
+        o2, l2 = fa.fa_fwd(q, k, v, w.scale, causal, ref_win)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), (causal, win)
+        assert torch.equal(l1, l2)
+    o, lse = fa.fa_fwd(q, k, v, w.scale, False, (big, big))
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_ref(bits(w.q), bits(w.k), bits(w.v), w.scale, False, (big, big))
+    check("huge window", o.cpu(), lse.cpu(), O, LSE)
+    p = workloads.random_paged(80, [300, 40], 8, 2, 128, 16, 30, 128, max_blocks=24)
+    a = run_decode(fa, p, window_left=big)
+    b = run_decode(fa, p, window_left=-1)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
 # -------------------------------------------------------------------- varlen
 VARLEN_CASES = [
     ([1, 0, 7, 128, 129, 300], 4, 2, 128, True, (-1, -1)),
