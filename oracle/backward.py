@@ -91,12 +91,15 @@ def attention_bwd_query_rows_ref(q, k, v, dout, b, h, rows, softmax_scale=None, 
 
 
 def attention_bwd_key_rows_ref(q, k, v, dout, b, g, keys, softmax_scale=None, causal=False,
-                               window=(-1, -1), row_block=1024):
+                               window=(-1, -1), row_block=1024, row_start=0):
     """dK and dV of selected key rows of one (batch, KV head g): (n, d) each.
 
     Every query row of every query head of the group contributes, so all rows
     are visited (in blocks); each block's P is formed over all keys (the row
     normalisation needs them) and only the selected key columns are kept.
+    Rows before ``row_start`` are skipped: pass it only when those rows see
+    none of the selected keys (e.g. causal, row_start <= min(keys) - (Lk - Lq)),
+    so that their contribution is zero.
     """
     B, Lq, Hq, d = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
@@ -107,7 +110,7 @@ def attention_bwd_key_rows_ref(q, k, v, dout, b, g, keys, softmax_scale=None, ca
     dv = np.zeros((keys.size, v.shape[3]))
     group = Hq // Hkv
     for h in range(g * group, (g + 1) * group):
-        for r0 in range(0, Lq, row_block):
+        for r0 in range(row_start, Lq, row_block):
             rows = np.arange(r0, min(Lq, r0 + row_block))
             vis = key_visibility(Lq, Lk, causal, window[0], window[1], rows=rows)
             qr, dr = _f64(q[b, rows, h]), _f64(dout[b, rows, h])

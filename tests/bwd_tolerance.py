@@ -85,7 +85,7 @@ def query_rows_tolerance(q, k, v, dout, b, h, rows, scale, causal, window, ref_r
 
 
 def key_rows_tolerance(q, k, v, dout, b, g, keys, scale, causal, window, ref_dk, ref_dv,
-                       row_block=1024):
+                       row_block=1024, row_start=0):
     """Tolerances of dK and dV at selected keys of one (batch, KV head)."""
     B, Lq, Hq, d = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
@@ -95,7 +95,7 @@ def key_rows_tolerance(q, k, v, dout, b, g, keys, scale, causal, window, ref_dk,
     bK = np.zeros((keys.size, d))
     bV = np.zeros((keys.size, v.shape[3]))
     for h in range(g * G, (g + 1) * G):
-        for r0 in range(0, Lq, row_block):
+        for r0 in range(row_start, Lq, row_block):
             rows = np.arange(r0, min(Lq, r0 + row_block))
             vis = oracle.key_visibility(Lq, Lk, causal, window[0], window[1], rows=rows)
             qr, dr = _f64(q[b, rows, h]), _f64(dout[b, rows, h])

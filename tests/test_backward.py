@@ -100,3 +100,33 @@ def test_bwd_huge_window_equals_unbounded(fa):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_bwd_full_causal_gqa_long_sampled(fa):
+    """The long-context GQA workload as bench.py times it (B=1, Hq=32, Hkv=8,
+    L=16384): dQ on sampled rows; dK, dV on sampled keys of the second half
+    (rows before a key never see it under the causal mask, so only rows from
+    the earliest sampled key on are summed)."""
+    w = workloads.causal_gqa_long()
+    B, L, Hq, d = w.q.shape
+    dout = workloads.upstream_grad(1003, (B, L, Hq, d))
+    dq, dk, dv = run_bwd(fa, w, dout)
+    qb, kb, vb, db = bits(w.q), bits(w.k), bits(w.v), bits(dout)
+    rng = np.random.default_rng(13)
+    for h in (0, 3, 29):
+        rows = np.unique(np.concatenate([[0, 127, 128, 8191, 16383], rng.integers(0, L, 4)]))
+        ref = oracle.attention_bwd_query_rows_ref(qb, kb, vb, db, 0, h, rows, w.scale, True)
+        tol = query_rows_tolerance(qb, kb, vb, db, 0, h, rows, w.scale, True, (-1, -1), ref)
+        x = ratio(f64(dq[0, rows, h]), ref, tol)
+        print(f"[parity] bwd gqa-long dq h{h}: max err/tol {x:.3f}", flush=True)
+        assert x <= 1.0
+    for g in (0, 7):
+        keys = np.unique(np.concatenate([[14336, 15999, 16256, 16383], rng.integers(14336, L, 4)]))
+        start = int(keys.min())
+        rk, rv = oracle.attention_bwd_key_rows_ref(qb, kb, vb, db, 0, g, keys, w.scale, True,
+                                                   row_start=start)
+        tk, tv = key_rows_tolerance(qb, kb, vb, db, 0, g, keys, w.scale, True, (-1, -1), rk, rv,
+                                    row_start=start)
+        xk, xv = ratio(f64(dk[0, keys, g]), rk, tk), ratio(f64(dv[0, keys, g]), rv, tv)
+        print(f"[parity] bwd gqa-long dk/dv g{g}: max err/tol {xk:.3f} / {xv:.3f}", flush=True)
+        assert xk <= 1.0 and xv <= 1.0

@@ -162,6 +162,14 @@ def test_selected_rows_and_keys_match_the_full_gradient():
                                                    row_block=16)
         assert np.abs(dk - dK[1, keys, 1]).max() < 1e-12
         assert np.abs(dv - dV[1, keys, 1]).max() < 1e-12
+        if causal:
+            # rows before min(keys) - (Lk - Lq) see none of the keys: skipping them is exact
+            late = [40, 41, 59]
+            start = min(late) - (Lk - Lq)
+            dk2, dv2 = oracle.attention_bwd_key_rows_ref(q, k, v, do, 1, 1, late, 0.3, causal, window,
+                                                         row_block=16, row_start=start)
+            assert np.abs(dk2 - dK[1, late, 1]).max() < 1e-12
+            assert np.abs(dv2 - dV[1, late, 1]).max() < 1e-12
 
 
 def test_planted_mistakes_are_caught(monkeypatch):
