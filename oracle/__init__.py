@@ -70,6 +70,7 @@ from .backward import (
     attention_bwd_ref,
     attention_bwd_query_rows_ref,
     attention_bwd_key_rows_ref,
+    attention_varlen_bwd_ref,
 )
 
 __all__ = [
@@ -90,4 +91,5 @@ __all__ = [
     "attention_bwd_ref",
     "attention_bwd_query_rows_ref",
     "attention_bwd_key_rows_ref",
+    "attention_varlen_bwd_ref",
 ]

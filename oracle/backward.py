@@ -121,3 +121,24 @@ def attention_bwd_key_rows_ref(q, k, v, dout, b, g, keys, softmax_scale=None, ca
             dk += scale * (ds.T @ qr)
             dv += p[:, keys].T @ dr
     return dk, dv
+
+
+def attention_varlen_bwd_ref(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, softmax_scale=None,
+                             causal=False, window=(-1, -1), row_block=1024):
+    """dQ, dK, dV (float64) of packed varlen attention: q, dout (total_q, Hq, d),
+    k, v (total_k, Hkv, d).  Sequences never attend across each other, so the
+    gradient of sequence b is the dense gradient of its own slices."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    d = q.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dQ, dK, dV = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(cq) - 1):
+        qs, ks = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        if cq[b + 1] == cq[b] or ck[b + 1] == ck[b]:
+            continue    # no rows or no keys: every gradient of the sequence is 0
+        g = attention_bwd_ref(q[None, qs], k[None, ks], v[None, ks], dout[None, qs], scale,
+                              causal, window, row_block)
+        dQ[qs], dK[ks], dV[ks] = g[0][0], g[1][0], g[2][0]
+    return dQ, dK, dV

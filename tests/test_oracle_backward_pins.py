@@ -205,3 +205,45 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert fd_check((1, 5, 5, 4, 2, 3, False, (-1, -1))) > 1e-3
     monkeypatch.setattr(oracle_backward, "_kv_head", orig_map)
     assert max(fd_check(c) for c in cases) < 1e-7
+
+
+# ------------------------------------------------------------------ varlen
+def varlen_loss(q, k, v, do, cq, ck, scale, causal, window):
+    O, _ = oracle.attention_varlen_ref(q, k, v, cq, ck, scale, causal, window)
+    return float(np.sum(O * do))
+
+
+def test_varlen_matches_finite_differences():
+    # three sequences, one with no rows and one with Lk > Lq
+    lq, lk = [3, 0, 2], [2, 3, 4]
+    cq = np.concatenate([[0], np.cumsum(lq)]); ck = np.concatenate([[0], np.cumsum(lk)])
+    rng = np.random.default_rng(5)
+    q, k, v = rng.standard_normal((5, 2, 3)), rng.standard_normal((9, 1, 3)), rng.standard_normal((9, 1, 3))
+    do = rng.standard_normal((5, 2, 3))
+    got = oracle.attention_varlen_bwd_ref(q, k, v, do, cq, ck, 0.8, True, (2, -1))
+    h = 1e-6
+    for x, g in zip((q, k, v), got):
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            up = varlen_loss(q, k, v, do, cq, ck, 0.8, True, (2, -1))
+            x[idx] = old - h
+            dn = varlen_loss(q, k, v, do, cq, ck, 0.8, True, (2, -1))
+            x[idx] = old
+            assert abs((up - dn) / (2 * h) - g[idx]) < 1e-7
+
+
+def test_varlen_single_sequence_is_dense_and_sequences_are_isolated():
+    q, k, v, do = rand(30, 4, 8), rand(40, 2, 8), rand(40, 2, 8), rand(30, 4, 8)
+    got = oracle.attention_varlen_bwd_ref(q, k, v, do, [0, 30], [0, 40], 0.4, True)
+    want = oracle.attention_bwd_ref(q[None], k[None], v[None], do[None], 0.4, True)
+    for g, w in zip(got, want):
+        assert np.abs(g - w[0]).max() < 1e-13
+    # changing sequence 1's data leaves sequence 0's gradients unchanged
+    cq, ck = [0, 12, 30], [0, 15, 40]
+    a = oracle.attention_varlen_bwd_ref(q, k, v, do, cq, ck, 0.4, True)
+    q2, k2, v2, do2 = (x.copy() for x in (q, k, v, do))
+    q2[12:] += 1.0; k2[15:] -= 2.0; v2[15:] *= 3.0; do2[12:] += 0.5
+    b = oracle.attention_varlen_bwd_ref(q2, k2, v2, do2, cq, ck, 0.4, True)
+    assert np.array_equal(a[0][:12], b[0][:12]) and np.array_equal(a[1][:15], b[1][:15])
+    assert np.array_equal(a[2][:15], b[2][:15])
