@@ -277,6 +277,26 @@ def bench_bwd(fa, args):
                                      "flops": fb3}
         del a, do3, o3, l3, ws3, g3, w3
         torch.cuda.empty_cache()
+        # varlen + sliding-window backward (the varlen window workload, d = 64)
+        w5 = workloads.varlen_window()
+        a = [t.cuda() for t in (w5.q, w5.k, w5.v)]
+        cu5 = torch.from_numpy(w5.cu_seqlens).cuda()
+        do5 = workloads.upstream_grad(1005, tuple(w5.q.shape)).cuda()
+        o5, l5 = fa.fa_fwd_varlen(*a, cu5, cu5, w5.max_seqlen, w5.max_seqlen, w5.scale, True,
+                                  w5.window)
+        ws5 = torch.empty(fa.fa_bwd_varlen_workspace_size(len(w5.lens), 16, int(w5.cu_seqlens[-1])),
+                          dtype=torch.uint8, device="cuda")
+        g5 = [torch.empty_like(t) for t in a]
+        fb5 = 2.5 * varlen_flops(w5)
+        ms = time_calls(lambda: fa.fa_bwd_varlen(*a, o5, l5, do5, cu5, cu5, w5.max_seqlen,
+                                                 w5.max_seqlen, w5.scale, True, w5.window,
+                                                 dq=g5[0], dk=g5[1], dv=g5[2], workspace=ws5),
+                        max(20, args.steps // 4), args.warmup, args.prewarm_ms)
+        wl["bwd_varlen_window"] = {"ms": round(ms, 4), "TFLOP/s": round(fb5 / ms / 1e9, 2),
+                                   "frac_mfma": round(fb5 / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                   "flops": fb5}
+        del a, cu5, do5, o5, l5, ws5, g5, w5
+        torch.cuda.empty_cache()
     return wl
 
 

@@ -45,6 +45,10 @@ _EXPORTS = {
                                                   ctypes.c_int] + _MODS + [ctypes.c_void_p]),
     "fa_decode_paged_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 6),
     "fa_bwd_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 3),
+    "fa_bwd_varlen_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 3),
+    "fa_bwd_varlen": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_int] * 8
+                      + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fa_bwd": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6
                + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -398,6 +402,50 @@ def fa_bwd(q, k, v, out, lse, dout, softmax_scale=None, causal=False, window=(-1
     return dq, dk, dv
 
 
+def fa_bwd_varlen_workspace_size(B, Hq, total_q):
+    return int(load_library().fa_bwd_varlen_workspace_size(B, Hq, total_q))
+
+
+def fa_bwd_varlen(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                  max_seqlen_k, softmax_scale=None, causal=False, window=(-1, -1), dq=None,
+                  dk=None, dv=None, workspace=None, stream=None):
+    """Backward of fa_fwd_varlen: q, out, dout (total_q, Hq, d), k, v (total_k, Hkv, d),
+    lse (Hq, total_q) from fa_fwd_varlen, cu_seqlens int32 device tensors -> dq, dk, dv."""
+    torch = _torch()
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, nm, torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    if tuple(k.shape) != (total_k, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be (total_k, Hkv, d)")
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("out and dout must have q's shape")
+    if tuple(lse.shape) != (Hq, total_q):
+        raise ValueError("lse must be (Hq, total_q)")
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        need = fa_bwd_varlen_workspace_size(B, Hq, total_q)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B,
+                           int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, Hq, Hkv, d,
+                           scale, int(bool(causal)), int(window[0]), int(window[1]),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(stream))
+    _check("fa_bwd_varlen", st)
+    return dq, dk, dv
+
+
 def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, v_new=None,
                    softmax_scale=None, causal=True, window=(-1, -1), out=None, lse=None,
                    return_lse=True, stream=None, softcap=0.0, alibi_slopes=None):
@@ -445,6 +493,6 @@ def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, 
 __all__ = ["fa_fwd", "fa_fwd_varlen", "fa_varlen_plan", "fa_fwd_varlen_run",
            "fa_decode_paged", "fa_decode_plan", "fa_decode_paged_run",
            "fa_decode_paged_workspace_size", "fa_fwd_kvcache", "fa_bwd",
-           "fa_bwd_workspace_size",
+           "fa_bwd_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
            "load_library", "exported_symbols", "cu_seqlens_from_lengths",
            "lengths_from_cu_seqlens", "FAError", "LIB_PATH"]

@@ -68,35 +68,67 @@ template <int D> struct BLds {
   }
 };
 
-// Float offset of row i's lse2 in the statistics of (b, h); its delta is 64
-// floats further.
-FA_DEV int64_t stat_offset(const BwdParams& p, int b, int h, int i) {
-  return ((int64_t)(b * p.Hq + h) * (p.Lq_pad / kBwdStatRows) + i / kBwdStatRows) *
-             (2 * kBwdStatRows) + (i % kBwdStatRows);
+// Float offset of statistics row r's lse2; its delta is 64 floats further.
+// Every (batch, head) or (sequence, head) starts at a multiple of 64 rows.
+FA_DEV int64_t stat_offset(int64_t r) {
+  return (r / kBwdStatRows) * (2 * kBwdStatRows) + (r % kBwdStatRows);
+}
+
+// First statistics row of (batch b, head h) (dense), or of sequence b of
+// head h, whose tile slots start at t_b (varlen).
+template <bool VARLEN>
+FA_DEV int64_t stat_base(const BwdParams& p, int b, int h, int t_b) {
+  return VARLEN ? (int64_t)h * p.stat_rows + (int64_t)t_b * kBlockM
+                : (int64_t)(b * p.Hq + h) * p.Lq_pad;
+}
+
+// Sequence owning tile slot t when sequence b's slots start at
+// floor(cu[b] / tile) + b (binary search over the cumulative offsets).
+FA_DEV int slot_sequence(const int* cu, int B, int t, int tile) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] / tile + mid <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 }  // namespace
 
-// One group of D/8 lanes per (batch, head, row), rows padded to Lq_pad, so
-// consecutive groups write consecutive statistics:
-// delta = sum_d dO * O in fp32 (fixed order), lse2 = LSE * log2(e), or +inf
-// for a row with no visible key (LSE = -inf) and for padding rows, so that
-// exp2(x - lse2) = 0 there.
-template <int D>
+// One group of D/8 lanes per statistics row, in row order, so consecutive
+// groups write consecutive statistics: delta = sum_d dO * O in fp32 (fixed
+// order), lse2 = LSE * log2(e), or +inf for a row with no visible key
+// (LSE = -inf) and for padding rows, so that exp2(x - lse2) = 0 there.
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(256)
 void bwd_prep_kernel(BwdParams p) {
   constexpr int KCH = D / 8;
-  // B * Hq * Lq_pad < 2^28 (the statistics are < 2^31 bytes): 32-bit indices
+  // all statistics rows < 2^28 (the statistics are < 2^31 bytes): 32-bit indices
   const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
   const uint32_t row = gid / KCH;
   const int ch = (int)(gid % KCH);
-  if (row >= (uint32_t)(p.B * p.Hq * p.Lq_pad)) return;   // whole KCH-lane groups exit together
-  const uint32_t bh = row / (uint32_t)p.Lq_pad;
-  const int i = (int)(row - bh * (uint32_t)p.Lq_pad);
-  const int b = (int)(bh / (uint32_t)p.Hq), h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
+  const uint32_t rows_per_head = VARLEN ? (uint32_t)p.stat_rows : (uint32_t)p.Lq_pad;
+  if (row >= (uint32_t)(VARLEN ? p.Hq : p.B * p.Hq) * rows_per_head) return;   // whole groups exit together
+  const uint32_t bh = row / rows_per_head;
+  const int r = (int)(row - bh * rows_per_head);
+  int b, h, i, lq;
+  int64_t tok;       // token index of the row (varlen: in the packed batch)
+  if (VARLEN) {
+    h = (int)bh;
+    b = slot_sequence(p.cu_q, p.B, r / kBlockM, kBlockM);
+    i = r - (p.cu_q[b] / kBlockM + b) * kBlockM;
+    lq = p.cu_q[b + 1] - p.cu_q[b];
+    tok = (int64_t)p.cu_q[b] + i;
+  } else {
+    b = (int)(bh / (uint32_t)p.Hq);
+    h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
+    i = r;
+    lq = p.Lq;
+    tok = (int64_t)b * p.Lq + i;
+  }
   float s = 0.f;
-  if (i < p.Lq) {
-    const int64_t off = (int64_t)b * p.q_batch_stride + (int64_t)i * p.q_tok_stride + (int64_t)h * D + 8 * ch;
+  if (i < lq) {
+    const int64_t off = tok * p.q_tok_stride + (int64_t)h * D + 8 * ch;
     const u32x4 a = *reinterpret_cast<const u32x4*>(p.dout + off);
     const u32x4 o = *reinterpret_cast<const u32x4*>(p.o + off);
 #pragma unroll
@@ -106,11 +138,12 @@ void bwd_prep_kernel(BwdParams p) {
   for (int m = KCH / 2; m > 0; m >>= 1) s += __shfl_xor(s, m);
   if (ch == 0) {
     float l2 = INFINITY;
-    if (i < p.Lq) {
-      const float l = p.lse[((int64_t)b * p.Hq + h) * p.Lq + i];
+    if (i < lq) {
+      const float l = VARLEN ? p.lse[(int64_t)h * p.lse_seq_stride + tok]
+                             : p.lse[((int64_t)b * p.Hq + h) * p.lse_seq_stride + i];
       l2 = l == -INFINITY ? INFINITY : l * kLog2eF;
     }
-    const int64_t so = stat_offset(p, b, h, i);
+    const int64_t so = stat_offset(row);
     p.stat[so] = l2;
     p.stat[so + kBwdStatRows] = s;
   }
@@ -124,7 +157,7 @@ void bwd_prep_kernel(BwdParams p) {
 // the MFMA work of a block splits evenly between the pair.
 constexpr int kDkdvThreads = 512;
 
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(kDkdvThreads, 1)
 void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KSTEPS = D / 16;                 // MFMA steps over d
@@ -149,9 +182,25 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   // ---- work item: (batch b, KV head g, key tile kt), early key tiles (which
   // the most causal rows see) first; with the XCD-aware order all key tiles
-  // of a KV group run on one XCD, so its Q and dO stay in that L2.
+  // of a KV group run on one XCD, so its Q and dO stay in that L2.  Varlen:
+  // key tile slots of sequence b start at floor(cu_k[b] / 128) + b.
   int b, g, kt;
-  {
+  int Lq = p.Lq, Lk = p.Lk;
+  int64_t q_tok0 = 0, k_tok0 = 0;   // first token of the sequence (varlen)
+  int t_b = 0;                      // first query tile slot of the sequence (varlen)
+  if (VARLEN) {
+    const int id = blockIdx.x;
+    g = id % p.Hkv;
+    const int t = id / p.Hkv;
+    b = slot_sequence(p.cu_k, p.B, t, kBwdKeys);
+    kt = t - (p.cu_k[b] / kBwdKeys + b);
+    q_tok0 = p.cu_q[b];
+    k_tok0 = p.cu_k[b];
+    Lq = p.cu_q[b + 1] - p.cu_q[b];
+    Lk = p.cu_k[b + 1] - p.cu_k[b];
+    t_b = p.cu_q[b] / kBlockM + b;
+    if (kt * kBwdKeys >= Lk) return;   // a spare slot: no keys (uniform per workgroup)
+  } else {
     const int id = blockIdx.x;
     if (p.xcd_groups > 0) {
       const int x = id & 7, s = id >> 3;
@@ -166,8 +215,10 @@ void bwd_dkdv_kernel(BwdParams p) {
       b = r / p.Hkv;
       g = r - b * p.Hkv;
     }
+    q_tok0 = (int64_t)b * p.Lq;
+    k_tok0 = (int64_t)b * p.Lk;
   }
-  const int Lq = p.Lq, Lk = p.Lk, delta = Lk - Lq;
+  const int delta = Lk - Lq;
   const int k0 = kt * kBwdKeys;
   const int kw0 = k0 + 32 * blk;
   const int key = kw0 + n;
@@ -175,10 +226,10 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   // ---- resident operand (B): K^T (role 0) or V^T (role 1); lane (key n,
   // half hi) holds d = 16t + 8hi + 0..7 of its key; keys past Lk read zeros.
-  const int64_t kv_off = (int64_t)b * p.k_batch_stride + (int64_t)g * D;
+  const int64_t kv_off = k_tok0 * p.k_tok_stride + (int64_t)g * D;
   u32x4 rf[KSTEPS];
   {
-    const uint32_t kbytes = (uint32_t)(((int64_t)(Lk - 1) * p.k_tok_stride + D) * 2);
+    const uint32_t kbytes = (uint32_t)(((int64_t)(Lk - 1) * p.k_tok_stride + D) * 2);   // Lk >= 1 here
     const __amdgpu_buffer_rsrc_t rr = make_rsrc((role == 0 ? p.k : p.v) + kv_off, kbytes);
     const uint32_t off = key < Lk ? (uint32_t)((int64_t)key * p.k_tok_stride + 8 * hi) * 2u : kOob;
 #pragma unroll
@@ -220,7 +271,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   // zeros.  Wave 0 also loads the tile's 64 lse2 and 64 delta values (512
   // contiguous bytes of the statistics; lanes 32-63 load zeros).
   const uint32_t q_row_bytes = (uint32_t)(p.q_tok_stride * 2);
-  const uint32_t q_bytes = (uint32_t)(((int64_t)(Lq - 1) * p.q_tok_stride + D) * 2);
+  const uint32_t q_bytes = Lq > 0 ? (uint32_t)(((int64_t)(Lq - 1) * p.q_tok_stride + D) * 2) : 0u;
   uint32_t src;
   {
     const int r = wave * RPI + lane / KCH, slot = lane % KCH;
@@ -229,9 +280,10 @@ void bwd_dkdv_kernel(BwdParams p) {
   const uint32_t q_lds_addr = lds_address(q_lds), do_lds_addr = lds_address(do_lds);
   const uint32_t st_lds_addr = lds_address(st_lds);
   const uint32_t wave_lds = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 1024);
-  const uint16_t* qb = p.q + (int64_t)b * p.q_batch_stride;
-  const uint16_t* dob = p.dout + (int64_t)b * p.q_batch_stride;
-  const uint32_t stat_bytes = (uint32_t)((int64_t)p.B * p.Hq * p.Lq_pad * 2 * 4);
+  const uint16_t* qb = p.q + q_tok0 * p.q_tok_stride;
+  const uint16_t* dob = p.dout + q_tok0 * p.q_tok_stride;
+  const uint32_t stat_bytes = (uint32_t)((int64_t)(VARLEN ? p.Hq : p.B * p.Hq) *
+                                         (VARLEN ? p.stat_rows : p.Lq_pad) * 2 * 4);
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.stat, stat_bytes);
   const uint32_t st_src = lane < 32 ? 16u * lane : kOob;
   auto fetch = [&](int s, int buf) {
@@ -247,7 +299,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       lds_load16(dr, src, soff, do_lds_addr + buf * TILE_BYTES + wave_lds + 8192u * i);
     }
     if (wave == 0) {
-      const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)(stat_offset(p, b, hh, qt * 64) * 4));
+      const int64_t sr = stat_base<VARLEN>(p, b, hh, t_b) + qt * 64;
+      const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)(stat_offset(sr) * 4));
       lds_load16(srs, st_src, so, st_lds_addr + buf * 1024u);
     }
   };
@@ -383,7 +436,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(kPrefillThreads, 2)
 void bwd_dq_kernel(BwdParams p) {
   constexpr int KSTEPS = D / 16;
@@ -401,11 +454,14 @@ void bwd_dq_kernel(BwdParams p) {
   const int n = lane & 31, hi = lane >> 5;
   const int i16 = lane & 15, g16 = lane >> 4;
 
-  const WorkItem w = map_work_dense(p, blockIdx.x);
-  const int Lq = p.Lq, Lk = p.Lk, delta = Lk - Lq;
+  const WorkItem w = VARLEN ? map_work_varlen(p, blockIdx.x) : map_work_dense(p, blockIdx.x);
+  if (!w.valid) return;    // a spare varlen slot (uniform per workgroup)
+  const int Lq = w.Lq, Lk = w.Lk, delta = Lk - Lq;
   const int kvh = w.h / p.group;
-  const int64_t q_off = (int64_t)w.b * p.q_batch_stride + (int64_t)w.h * D;
-  const int64_t kv_off = (int64_t)w.b * p.k_batch_stride + (int64_t)kvh * D;
+  const int64_t q_tok0 = VARLEN ? (int64_t)w.q_base : (int64_t)w.b * p.Lq;
+  const int64_t k_tok0 = VARLEN ? (int64_t)w.k_base : (int64_t)w.b * p.Lk;
+  const int64_t q_off = q_tok0 * p.q_tok_stride + (int64_t)w.h * D;
+  const int64_t kv_off = k_tok0 * p.k_tok_stride + (int64_t)kvh * D;
 
   // ---- key range of the workgroup and of this wave (as in the forward) ----
   const int q0 = w.qt * kBlockM;
@@ -431,7 +487,7 @@ void bwd_dq_kernel(BwdParams p) {
   // ---- resident Q^T and dO^T (B operand), the row's lse2 and delta --------
   u32x4 qf[KSTEPS], dof[KSTEPS];
   {
-    const uint32_t qbytes = (uint32_t)(((int64_t)(Lq - 1) * p.q_tok_stride + D) * 2);
+    const uint32_t qbytes = (uint32_t)(((int64_t)(Lq - 1) * p.q_tok_stride + D) * 2);   // Lq >= 1 here
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + q_off, qbytes);
     const __amdgpu_buffer_rsrc_t dr = make_rsrc(p.dout + q_off, qbytes);
     const uint32_t off = row < Lq ? (uint32_t)(row * p.q_tok_stride + 8 * hi) * 2u : kOob;
@@ -441,12 +497,13 @@ void bwd_dq_kernel(BwdParams p) {
       dof[t] = buf_load16(dr, off + 32u * t);
     }
   }
-  const int64_t so = stat_offset(p, w.b, w.h, row);      // row < Lq_pad
+  // the tile's rows lie in the sequence's padded statistics
+  const int64_t so = stat_offset(stat_base<VARLEN>(p, w.b, w.h, VARLEN ? w.q_base / kBlockM + w.b : 0) + row);
   const float lse2 = p.stat[so], dlt = p.stat[so + kBwdStatRows];
 
   // ---- staging of K/V tiles (as in the forward, one swizzle for both) -----
   const uint32_t k_row_bytes = (uint32_t)(p.k_tok_stride * 2);
-  const uint32_t k_bytes = (uint32_t)(((int64_t)(Lk - 1) * p.k_tok_stride + D) * 2);
+  const uint32_t k_bytes = Lk > 0 ? (uint32_t)(((int64_t)(Lk - 1) * p.k_tok_stride + D) * 2) : 0u;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + kv_off, k_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + kv_off, k_bytes);
   uint32_t src;
@@ -561,23 +618,27 @@ void bwd_dq_kernel(BwdParams p) {
   }
 }
 
-template <int D>
+template <int D, bool VARLEN>
 static hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  const int64_t prep_threads = (int64_t)p.B * p.Lq_pad * p.Hq * (D / 8);
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0,
-                     stream, p);
+  const int64_t stat_rows = VARLEN ? (int64_t)p.Hq * p.stat_rows : (int64_t)p.B * p.Hq * p.Lq_pad;
+  const int64_t prep_threads = stat_rows * (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<D, VARLEN>), dim3((unsigned)((prep_threads + 255) / 256)),
+                     dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(p.B * p.Hkv * p.num_k_tiles)),
-                     dim3(kDkdvThreads), 0, stream, p);
+  const int64_t kv_blocks = (int64_t)(VARLEN ? 1 : p.B) * p.Hkv * p.num_k_tiles;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, VARLEN>), dim3((unsigned)kv_blocks), dim3(kDkdvThreads), 0,
+                     stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(p.B * p.Hq * p.num_q_tiles)),
-                     dim3(kPrefillThreads), 0, stream, p);
+  const int64_t q_blocks = (int64_t)(VARLEN ? 1 : p.B) * p.Hq * p.num_q_tiles;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, VARLEN>), dim3((unsigned)q_blocks), dim3(kPrefillThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream) {
-  return d == 128 ? launch_bwd_d<128>(p, stream) : launch_bwd_d<64>(p, stream);
+hipError_t launch_bwd(const BwdParams& p, int d, bool varlen, hipStream_t stream) {
+  if (varlen) return d == 128 ? launch_bwd_d<128, true>(p, stream) : launch_bwd_d<64, true>(p, stream);
+  return d == 128 ? launch_bwd_d<128, false>(p, stream) : launch_bwd_d<64, false>(p, stream);
 }
 
 }  // namespace fa

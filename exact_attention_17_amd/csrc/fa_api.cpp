@@ -431,6 +431,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
   p.stat = static_cast<float*>(workspace);
+  p.lse_seq_stride = Lq;
   p.B = B; p.Lq = Lq; p.Lk = Lk;
   p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
   p.Lq_pad = (int)(cdiv(Lq, fa::kBlockM) * fa::kBlockM);
@@ -448,7 +449,73 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if ((int64_t)p.num_q_tiles * B * Hq >= kMaxElems || (int64_t)p.num_k_tiles * B * Hkv >= kMaxElems)
     return FA_ERR_INVALID_ARG;
   if ((int64_t)B * p.Lq_pad * Hq * (d / 8) >= ((int64_t)1 << 40)) return FA_ERR_INVALID_ARG;
-  hipError_t e = fa::launch_bwd(p, d, static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_bwd(p, d, false, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_varlen_workspace_size(int B, int Hq, int total_q) {
+  if (B < 1 || Hq < 1 || total_q < 0) return 0;
+  // tile slots: sequence b owns [cu_q[b]/128 + b, cu_q[b+1]/128 + b + 1)
+  const int64_t rows = ((int64_t)total_q / fa::kBlockM + B) * fa::kBlockM;
+  const int64_t bytes = (int64_t)Hq * rows * 2 * (int64_t)sizeof(float);
+  if (bytes >= ((int64_t)1 << 31)) return 0;
+  return (size_t)bytes;
+}
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int Hq,
+                        int Hkv, int d, float softmax_scale, int causal, int window_left,
+                        int window_right, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  fa_status st = check_common(Hq, Hkv, d, softmax_scale, causal, window_left, window_right);
+  if (st != FA_OK) return st;
+  if ((st = check_tensors(q, k, v, o, lse)) != FA_OK) return st;
+  if (!lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return FA_ERR_INVALID_ARG;
+  if (!cu_seqlens_q || !cu_seqlens_k || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return FA_ERR_INVALID_ARG;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FA_ERR_INVALID_ARG;
+  if ((int64_t)total_q * Hq * d >= kMaxBatchElems || (int64_t)total_k * Hkv * d >= kMaxBatchElems)
+    return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_varlen_workspace_size(B, Hq, total_q);
+  if (need == 0) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (total_q == 0 && total_k == 0) return FA_OK;
+
+  fa::BwdParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.stat = static_cast<float*>(workspace);
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.lse_seq_stride = total_q;
+  p.B = B; p.Lq = max_seqlen_q; p.Lk = max_seqlen_k;
+  p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.q_tok_stride = (int64_t)Hq * d;
+  p.k_tok_stride = (int64_t)Hkv * d;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.scale = softmax_scale;
+  p.causal = causal; p.win_left = norm_window(window_left); p.win_right = norm_window(window_right);
+  // tile slots, as for the forward: sequence b's start at floor(cu[b] / tile) + b
+  p.num_q_tiles = total_q / fa::kBlockM + B;
+  p.num_k_tiles = total_k / fa::kBwdKeys + B;
+  p.stat_rows = p.num_q_tiles * fa::kBlockM;
+  p.xcd_groups = xcd_groups(Hkv);
+  if ((int64_t)p.num_q_tiles * Hq >= kMaxElems || (int64_t)p.num_k_tiles * Hkv >= kMaxElems)
+    return FA_ERR_INVALID_ARG;
+  hipError_t e = fa::launch_bwd(p, d, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

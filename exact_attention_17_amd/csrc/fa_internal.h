@@ -70,7 +70,7 @@ struct AppendParams {
 // rows padded to a multiple of kBlockM (padded rows: lse2 = +inf, delta = 0).
 constexpr int kBwdStatRows = 64;
 struct BwdParams {
-  const uint16_t* q;       // (B, Lq, Hq, d) bf16 bits
+  const uint16_t* q;       // (B, Lq, Hq, d) bf16 bits; varlen: (total_q, Hq, d)
   const uint16_t* k;       // (B, Lk, Hkv, d)
   const uint16_t* v;
   const uint16_t* o;       // forward output (B, Lq, Hq, d)
@@ -80,14 +80,22 @@ struct BwdParams {
   uint16_t* dk;            // (B, Lk, Hkv, d)
   uint16_t* dv;
   float* stat;             // workspace: lse2 = lse * log2(e) (+inf for rows with no key), delta = dO . O
-  int B, Lq, Lk, Hq, Hkv, group;
-  int Lq_pad;              // ceil(Lq / kBlockM) * kBlockM
+  const int* cu_q;         // varlen: cumulative sequence offsets (device), else null
+  const int* cu_k;
+  const int* plan;         // always null (the shared varlen work map takes a plan)
+  int B, Lq, Lk, Hq, Hkv, group;   // varlen: Lq, Lk unused
+  int Lq_pad;              // dense: ceil(Lq / kBlockM) * kBlockM
+  // Statistics rows: dense, (batch b, head h) owns rows from (b * Hq + h) *
+  // Lq_pad; varlen, head h owns stat_rows = num_q_tiles * kBlockM rows from
+  // h * stat_rows, sequence b's starting (cu_q[b] / kBlockM + b) * kBlockM later.
+  int stat_rows;
+  int lse_seq_stride;      // dense Lq (lse (B, Hq, Lq)); varlen total_q (lse (Hq, total_q))
   int64_t q_tok_stride, k_tok_stride, q_batch_stride, k_batch_stride;
   float scale_log2;        // softmax_scale * log2(e)
   float scale;
   int causal, win_left, win_right;
-  int num_q_tiles;         // ceil(Lq / kBlockM): dQ workgroups per (batch, head)
-  int num_k_tiles;         // ceil(Lk / kBwdKeys): dK/dV workgroups per (batch, KV head)
+  int num_q_tiles;         // dense ceil(Lq / kBlockM) per (batch, head); varlen total tile slots
+  int num_k_tiles;         // dense ceil(Lk / kBwdKeys) per (batch, KV head); varlen total slots
   int xcd_groups, chunk_groups;
 };
 constexpr int kBwdKeys = 128;    // keys per dK/dV workgroup (4 waves x 32)
@@ -116,6 +124,6 @@ hipError_t launch_prefill(const PrefillParams& p, int d, int mode, hipStream_t s
 hipError_t launch_append(const AppendParams& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, int rows, hipStream_t stream);
 // row statistics, then dK/dV, then dQ, in stream order
-hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, bool varlen, hipStream_t stream);
 
 }  // namespace fa

@@ -83,54 +83,6 @@ template <int D> struct Lds {
   FA_DEV static int vswz(int r) { return D == 128 ? ((r & 1) * 6) ^ (((r >> 1) & 1) * 12) : 2 * (r & 3); }
 };
 
-// Varlen: without a plan, tile slots of sequence b start at
-// T_b = floor(cu_q[b] / 128) + b, which leaves room for its ceil(len_b / 128)
-// tiles before T_{b+1}; with a plan, slot t is the plan's item t.
-__device__ __forceinline__ WorkItem map_work_varlen(const PrefillParams& p, int id) {
-  WorkItem w;
-  const int r = id % p.Hq, t = id / p.Hq;
-  if (p.xcd_groups > 0) {
-    const int x = r & 7, i = r >> 3;
-    const int kvh = x + 8 * (i / p.group);
-    w.h = kvh * p.group + (i % p.group);
-  } else {
-    w.h = r;
-  }
-  if (p.plan) {
-    // planned run: item t of the host plan names (sequence, query tile); the
-    // plan is uniform per workgroup, so read it through the scalar cache
-    const __attribute__((address_space(4))) int* pc =
-        (const __attribute__((address_space(4))) int*)p.plan;
-    const int b = pc[2 * t], qt = pc[2 * t + 1];
-    w.valid = b >= 0 && b < p.B;
-    if (!w.valid) return w;
-    w.b = b;
-    w.q_base = p.cu_q[b];
-    w.Lq = p.cu_q[b + 1] - w.q_base;
-    w.k_base = p.cu_k[b];
-    w.Lk = p.cu_k[b + 1] - w.k_base;
-    w.qt = qt;
-    // an item outside the sequence's tiles (a plan made for other lengths)
-    // computes nothing
-    w.valid = qt >= 0 && qt < (w.Lq + kBlockM - 1) / kBlockM;
-    return w;
-  }
-  int lo = 0, hi = p.B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.cu_q[mid] / kBlockM + mid <= t) lo = mid; else hi = mid - 1;
-  }
-  w.b = lo;
-  w.q_base = p.cu_q[lo];
-  w.Lq = p.cu_q[lo + 1] - w.q_base;
-  w.k_base = p.cu_k[lo];
-  w.Lk = p.cu_k[lo + 1] - w.k_base;
-  const int lt = t - (w.q_base / kBlockM + lo);
-  const int ntiles = (w.Lq + kBlockM - 1) / kBlockM;
-  w.valid = lt < ntiles;
-  w.qt = ntiles - 1 - lt;
-  return w;
-}
 
 }  // namespace
 

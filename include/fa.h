@@ -295,6 +295,29 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int Hkv, int d, float softmax_scale, int causal, int window_left,
                  int window_right, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward of fa_fwd_varlen (packed sequences, skill page sec. 3.4): as
+ * fa_bwd, per sequence, with the layouts of fa_fwd_varlen:
+ *   q, o, dout, dq : (total_q, Hq, d)    k, v, dk, dv : (total_k, Hkv, d)
+ *   lse : (Hq, total_q) float32 from fa_fwd_varlen
+ *   cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, total_q,
+ *   total_k : as for fa_fwd_varlen (device offsets; the same device-side
+ *       preconditions)
+ *   workspace : at least fa_bwd_varlen_workspace_size(B, Hq, total_q) bytes,
+ *       256-byte aligned.
+ * Rows of a sequence without keys get dQ = 0; keys of a sequence without
+ * rows (or that no row sees) get dK = dV = 0.  Deterministic, as fa_bwd.
+ */
+size_t fa_bwd_varlen_workspace_size(int B, int Hq, int total_q);
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int Hq,
+                        int Hkv, int d, float softmax_scale, int causal, int window_left,
+                        int window_right, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,3 +130,48 @@ def test_bwd_full_causal_gqa_long_sampled(fa):
         xk, xv = ratio(f64(dk[0, keys, g]), rk, tk), ratio(f64(dv[0, keys, g]), rv, tv)
         print(f"[parity] bwd gqa-long dk/dv g{g}: max err/tol {xk:.3f} / {xv:.3f}", flush=True)
         assert xk <= 1.0 and xv <= 1.0
+
+
+# ------------------------------------------------------------------ varlen
+VARLEN_BWD_CASES = [
+    # lens_q, lens_k (None: same), Hq, Hkv, d, causal, window
+    ([1, 0, 7, 128, 129, 300], None, 4, 2, 128, True, (-1, -1)),
+    ([250, 3, 64], None, 2, 1, 64, False, (-1, -1)),
+    ([513, 17], None, 8, 8, 128, False, (30, 30)),
+    ([100, 0, 260], [300, 50, 260], 4, 2, 128, True, (-1, -1)),    # Lk != Lq; no rows
+    ([300, 40], [0, 400], 4, 1, 64, True, (64, -1)),               # a sequence without keys
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_BWD_CASES, ids=lambda c: f"n{len(c[0])}-h{c[2]}-kv{c[3]}-d{c[4]}-c{int(c[5])}-w{c[6][0]}")
+def test_bwd_varlen_sweep(fa, case):
+    lq, lk, Hq, Hkv, d, causal, window = case
+    lk = lq if lk is None else lk
+    seed = 600 + sum(lq) + d
+    q, k, v, cq, ck = workloads.random_varlen_qk(seed, lq, lk, Hq, Hkv, d)
+    dout = workloads.upstream_grad(seed + 1, tuple(q.shape))
+    scale = 1.0 / np.sqrt(d)
+    cqd, ckd = dev(torch.from_numpy(cq)), dev(torch.from_numpy(ck))
+    mq, mk = max(lq), max(lk)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o, lse = fa.fa_fwd_varlen(qd, kd, vd, cqd, ckd, mq, mk, scale, causal, window)
+    got = fa.fa_bwd_varlen(qd, kd, vd, o, lse, dev(dout), cqd, ckd, mq, mk, scale, causal, window)
+    torch.cuda.synchronize()
+    qb, kb, vb, db = bits(q), bits(k), bits(v), bits(dout)
+    ref = oracle.attention_varlen_bwd_ref(qb, kb, vb, db, cq, ck, scale, causal, window)
+    # tolerance per sequence (the bound of the dense case on each sequence's slices)
+    tol = [np.full_like(r, 1e-5) for r in ref]
+    for b in range(len(lq)):
+        qs, ks = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        if lq[b] == 0 or lk[b] == 0:
+            continue
+        rb = tuple(x[None] for x in (ref[0][qs], ref[1][ks], ref[2][ks]))
+        tb = bwd_tolerance(qb[None, qs], kb[None, ks], vb[None, ks], db[None, qs], scale, causal,
+                           window, rb)
+        tol[0][qs], tol[1][ks], tol[2][ks] = tb[0][0], tb[1][0], tb[2][0]
+    for name, g, r, t in zip(("dq", "dk", "dv"), got, ref, tol):
+        g = f64(g.cpu())
+        assert np.isfinite(g).all(), name
+        x = ratio(g, r, t)
+        print(f"[parity] bwd varlen{case} {name}: max err/tol {x:.3f}", flush=True)
+        assert x <= 1.0, name

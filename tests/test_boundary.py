@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["fa_status_string", "fa_fwd", "fa_fwd_varlen", "fa_varlen_plan",
                             "fa_fwd_varlen_run", "fa_decode_paged_workspace_size",
                             "fa_decode_paged", "fa_decode_plan", "fa_decode_paged_run",
-                            "fa_fwd_kvcache", "fa_bwd", "fa_bwd_workspace_size"])
+                            "fa_fwd_kvcache", "fa_bwd", "fa_bwd_workspace_size",
+                            "fa_bwd_varlen", "fa_bwd_varlen_workspace_size"])
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(fa.exported_symbols()) == names
@@ -281,3 +282,33 @@ def test_bwd_workspace_size(lib):
     assert lib.fa_bwd_workspace_size(1, 1, 129) == 256 * 2 * 4
     assert lib.fa_bwd_workspace_size(0, 4, 100) == 0
     assert lib.fa_bwd_workspace_size(1 << 14, 4, 1 << 15) == 0
+
+
+def bwd_varlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, cq=P, ck=P, B=2, mq=10, mk=10,
+             tq=16, tk=16, Hq=4, Hkv=2, d=128, scale=0.1, causal=1, wl=-1, wr=-1, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                             a["dv"], a["cq"], a["ck"], a["B"], a["mq"], a["mk"], a["tq"], a["tk"],
+                             a["Hq"], a["Hkv"], a["d"], a["scale"], a["causal"], a["wl"], a["wr"],
+                             a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(do=None), INVALID),
+    (dict(dq=P + 8), INVALID), (dict(cq=None), INVALID), (dict(ck=P + 2), INVALID),
+    (dict(B=0), INVALID), (dict(tq=-1), INVALID), (dict(mq=20), INVALID), (dict(mk=-1), INVALID),
+    (dict(Hq=5), INVALID), (dict(d=96), UNSUPPORTED), (dict(wr=-3), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws=P + 32), WORKSPACE), (dict(wsb=100), WORKSPACE),
+])
+def test_bwd_varlen_rejects(lib, kw, code):
+    assert bwd_varlen(lib, **kw) == code
+
+
+def test_bwd_varlen_workspace_size(lib):
+    # rows: (total_q / 128 + B) tile slots of 128 per head, two floats each
+    assert lib.fa_bwd_varlen_workspace_size(2, 4, 16) == 4 * (0 + 2) * 128 * 2 * 4
+    assert lib.fa_bwd_varlen_workspace_size(3, 2, 300) == 2 * (2 + 3) * 128 * 2 * 4
+    assert lib.fa_bwd_varlen_workspace_size(0, 4, 16) == 0
+    # nothing to do: both totals 0 is accepted without a launch
+    assert bwd_varlen(lib, tq=0, tk=0, mq=0, mk=0) == OK

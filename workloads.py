@@ -234,6 +234,18 @@ def random_varlen(seed, lens, Hq, Hkv, d, causal=True, window=(-1, -1)):
     return Varlen(f"varlen_s{seed}", q, k, v, lens, cu, causal, window, 1.0 / math.sqrt(d))
 
 
+def random_varlen_qk(seed, lens_q, lens_k, Hq, Hkv, d):
+    """Small varlen case with separate query and key lengths per sequence.
+    Returns (q, k, v, cu_q, cu_k); draw order q, k, v."""
+    rng = np.random.default_rng(seed)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    q = bf16_normal(rng, (int(cu_q[-1]), Hq, d))
+    k = bf16_normal(rng, (int(cu_k[-1]), Hkv, d))
+    v = bf16_normal(rng, (int(cu_k[-1]), Hkv, d))
+    return q, k, v, cu_q, cu_k
+
+
 def random_paged(seed, lens, Hq, Hkv, d, page_size, pool_pages, split_tokens=512,
                  max_blocks=None, window_left=-1):
     """Small paged case with the same layout rules as ``paged_decode``."""
