@@ -179,7 +179,7 @@ def main():
                     help="first run a plain copy of known size (for byte-counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
 

@@ -24,7 +24,7 @@ Sources (pages on the subject, cited by title and section):
     -- argument shapes, causal / window_size, cu_seqlens, block_table, GQA,
     and k_new / v_new appended to a KV cache of cache_seqlens tokens.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   causal alignment is bottom-right; window bounds are inclusive; -1 means an
   unbounded window side; query head h uses KV head h // (Hq // Hkv); LSE is the
   natural-log log-sum-exp of the scaled scores; a row with no visible key has
