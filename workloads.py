@@ -203,6 +203,17 @@ def varlen_window(seed=5, nseq=16, H=16, d=64, lo=64, hi=8192, window=(4096, 0))
                   1.0 / math.sqrt(d))
 
 
+# ------------------------------------------------------- maximum sizes
+def device_normal(seed, shape, device="cuda"):
+    """N(0, 1) rounded to bf16, drawn on `device` by torch's generator seeded
+    with `seed` (fp32 normals, then RNE to bf16).  Used where numpy would be
+    too slow (tensors of 2^30 elements); tests copy the same tensor to the host
+    for the oracle."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
 # ------------------------------------------------------- backward inputs
 def upstream_grad(seed, shape):
     """Upstream gradient dO for the backward pass: N(0, 1) rounded to bf16
