@@ -420,8 +420,10 @@ void prefill_fwd_kernel(PrefillParams p) {
   // buffers of K(j) and V(j-2), whose last reads finished before the barrier
   // that ended step j-1.  Then one basic block holds the MFMAs of S^T(j+1)
   // and of P_{j-1} V_{j-1} and the softmax of tile j (P_j), interleaved.
-  // When the reference max must be raised (rare), P_{j-1} V_{j-1} is added
-  // first, O is rescaled and P_{j-1} cleared, so the block adds zeros.
+  // While some row has seen no key, the max is taken before the block; when
+  // it must be raised then, P_{j-1} V_{j-1} is added first, O is rescaled and
+  // P_{j-1} cleared, so the block adds zeros.  Afterwards the max is taken
+  // only when the tile shows a probability above 2^8 (rare).
   // (the parity of j, and so every LDS buffer offset, is a compile-time constant)
   auto step = [&](auto parity, int j, f32x16 (&Scur)[2], f32x16 (&Snxt)[2],
                   u32x4 (&Pprev)[4], u32x4 (&Pcur)[4]) {
@@ -429,18 +431,35 @@ void prefill_fwd_kernel(PrefillParams p) {
     const int kb = kb0 + j * kBlockN;
     modify(Scur, kb);
     mask_tile(Scur, kb);
-    update_max(Scur, [&] {
-      pv(nxt, Pprev);
+    // A row that has seen no key yet needs its max up front (its scores can
+    // lie anywhere).  Otherwise the max is only needed when a probability of
+    // the tile exceeds 2^8, which the growth of the row sum shows afterwards.
+    const bool exact = wave_any(m_ref == -INFINITY);
+    if (exact) {
+      update_max(Scur, [&] {
+        pv(nxt, Pprev);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Pprev[i] = u32x4{0u, 0u, 0u, 0u};
-    });
+        for (int i = 0; i < 4; ++i) Pprev[i] = u32x4{0u, 0u, 0u, 0u};
+      });
+    }
     const PageIds ik = page_ids(kb + 2 * kBlockN), iv = page_ids(kb);
     if (j + 2 < ntiles) fetch(krs, k_src, k_src_pg, kg, k_lds_addr + cur * TILE_BYTES, kb + 2 * kBlockN, ik);
     fetch(vrs, v_src, v_src_pg, vg, v_lds_addr + cur * TILE_BYTES, kb, iv);
+    const float la0 = l_a, lb0 = l_b;
     qk(nxt, Snxt);
     pv(nxt, Pprev);
     softmax(Scur, Pcur);
     interleave_hint();
+    // this lane's share of the tile's row sum bounds each of its probabilities
+    // (also catches inf/NaN): above 2^8, take back the tile, raise the max and
+    // rescale (P_{j-1} V_{j-1} is already in O, relative to the old max), and
+    // redo P_j (rare: wave-uniform branch)
+    if (!exact && wave_any(!((l_a - la0) + (l_b - lb0) <= 256.f))) {
+      l_a = la0;
+      l_b = lb0;
+      update_max(Scur, [] {});
+      softmax(Scur, Pcur);
+    }
     lds_load_wait();
     __syncthreads();
   };
