@@ -24,6 +24,11 @@
 //     per-wave LDS buffer; P*V runs on the fp32 VALU with V read in fully
 //     coalesced 256-byte rows.  The four waves merge in LDS and write one
 //     partial (O_s normalised, LSE_s) per query head.
+//   * decode_split_quad (d = 128, at most four query heads per KV head, page
+//     sizes that are multiples of 16): one workgroup per (request, split, four
+//     adjacent KV heads), so every load instruction reads 1 KB of contiguous
+//     cache memory (one token's rows of the four heads) instead of 256-byte
+//     pieces of four slots; the general kernel above serves the other shapes.
 //   * decode_merge: one wave per (request, query head) combines the
 //     partials by their LSE and writes bf16 O and fp32 LSE.
 //   * Keys at or past a request's length (and before its window) never reach
@@ -328,6 +333,226 @@ void decode_split_kernel(DecodeParams p) {
   }
 }
 
+// Four KV heads per workgroup (d = 128, at most four query heads per KV head,
+// page_size a multiple of 16).  The cache holds a token's rows of all KV heads
+// side by side, so heads 4x..4x+3 of one token are 1 KB of contiguous memory:
+// each load instruction reads exactly that (lane l: 16 bytes of head l/16),
+// instead of four 256-byte rows of one head in four different slots.  A wave
+// takes 16-token chunks; the 16 tokens lie in one page, so their page id is
+// one scalar load.  Scores: the A operand holds the 16 query rows of the four
+// heads (row 4h + j is query j of KV head h, zero when j >= group), and one
+// v_mfma_f32_16x16x32_bf16 chain per KV head h multiplies them with that
+// head's K rows; lanes 16h..16h+15 keep the result, which is exactly head h's
+// rows there.  P*V on the VALU: lane (h, c) holds d = 8c..8c+7 of head h for
+// each token, so its 4 x 8 output values need no cross-lane sum.
+constexpr int kQuadHeads = 4;
+constexpr int kQuadChunk = 16;   // tokens per wave iteration
+
+__global__ __launch_bounds__(kDecodeThreads, 2)
+void decode_split_quad_kernel(DecodeParams p) {
+  constexpr int D = 128, NH = kQuadHeads, CH = kQuadChunk, KT = D / 32;
+  constexpr int SEG = NH * D;        // elements of a token's four-head segment (1 KB)
+  constexpr int KST = SEG + 8;       // padded row of the per-wave K staging tile
+  static_assert(16 * D * 4 <= CH * KST * 2, "wave partial must fit its K tile");
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[4][CH * KST];
+  __shared__ __attribute__((aligned(16))) float p_lds[4][CH][16];
+  __shared__ float a_lds[4][16];
+  __shared__ float m_lds[4][16], l_lds[4][16];
+  auto o_part = [&](int w_) { return reinterpret_cast<float*>(&k_lds[w_][0]); };   // [16][D]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // grid = (head quad, split, request), or 1-D over (plan item, head quad)
+  // with the quads of one item adjacent
+  const int nquads = p.Hkv / NH;
+  int s, b, quad;
+  if (p.planned) {
+    const int item = blockIdx.x / nquads;
+    quad = blockIdx.x - item * nquads;
+    const __attribute__((address_space(4))) int* pc =
+        (const __attribute__((address_space(4))) int*)p.plan;
+    b = pc[2 * item];
+    s = pc[2 * item + 1];
+    if (b < 0 || b >= p.B || s < 0 || s >= p.max_splits) return;   // not an item of this batch
+  } else {
+    quad = blockIdx.x;
+    s = blockIdx.y;
+    b = blockIdx.z;
+  }
+  const int G = p.group;
+
+  const int len = p.seqlens[b];
+  const int lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
+  const int split_base = s * p.split_tokens;
+  const int k_beg = max(split_base, lo);
+  const int k_end = min(len, split_base + p.split_tokens);
+  if (k_beg >= k_end) return;
+
+  const int* bt = p.block_table + (int64_t)b * p.max_blocks;
+  const int64_t tok_stride = (int64_t)p.Hkv * D;    // elements between cache slots
+  const uint16_t* kcache = p.k_cache + (int64_t)quad * SEG + 8 * lane;
+  const uint16_t* vcache = p.v_cache + (int64_t)quad * SEG + 8 * lane;
+
+  // A operand: lane row i = lane % 16 (KV head i/4, query i%4), d = 32t + 8*(lane/16)
+  u32x4 qa[KT];
+  {
+    const int qi = lane & 15, qg = lane >> 4;
+    const bool ok = (qi & 3) < G;
+    const int qh = (quad * NH + (qi >> 2)) * G + (qi & 3);
+    const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + qh) * D + 8 * qg;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+      qa[t] = ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * t) : u32x4{0, 0, 0, 0};
+  }
+
+  // S layout: lane (key n = lane%16, head g = lane/16) holds head g's rows 0..3.
+  // PV layout: lane (head g = lane/16, d chunk dc = lane%16).
+  const int sn = lane & 15, sg = lane >> 4, dc = lane & 15;
+  float m_ref[4], l_part[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { m_ref[r] = -INFINITY; l_part[r] = 0.f; }
+  float oacc[4][8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oacc[r][e] = 0.f;
+
+  const float c = p.scale_log2;
+  const int nchunks = (k_end - split_base + CH - 1) / CH;
+  const int c0 = (k_beg - split_base) / CH;
+  uint16_t* kt = k_lds[wave];
+
+  for (int ch = c0 + wave; ch < nchunks; ch += 4) {
+    const int kc = split_base + ch * CH;               // kc < k_end <= len
+    const bool partial = kc < k_beg || kc + CH > k_end;   // wave-uniform
+    // the chunk's 16 tokens share one page (kc and page_size are multiples
+    // of 16); tokens outside [k_beg, k_end) are read but masked below
+    const int pid = __builtin_amdgcn_readfirstlane(bt[kc / p.page_size]);
+    const int64_t slot0 = (int64_t)pid * p.page_size + kc % p.page_size;
+    u32x4 kr[CH], vr[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      kr[i] = *reinterpret_cast<const u32x4*>(kcache + (slot0 + i) * tok_stride);
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      vr[i] = *reinterpret_cast<const u32x4*>(vcache + (slot0 + i) * tok_stride);
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+        if (!(kc + i >= k_beg && kc + i < k_end)) vr[i] = u32x4{0, 0, 0, 0};
+    }
+    // K through the wave's LDS tile into the B operand order
+#pragma unroll
+    for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(kt + i * KST + 8 * lane) = kr[i];
+    __builtin_amdgcn_wave_barrier();
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+        acc = mfma16x16x32(qa[t], *reinterpret_cast<const u32x4*>(kt + sn * KST + h * D + 32 * t + 8 * sg), acc);
+      if (sg == h) sacc = acc;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (partial && !(kc + sn >= k_beg && kc + sn < k_end))
+      sacc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // ---- online softmax per query row ------------------------------------
+    bool any_up = false;
+    float tmax[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      tmax[r] = row16_max(sacc[r]) * c;
+      any_up |= tmax[r] > m_ref[r] + kRescaleTau;
+    }
+    if (wave_any(any_up)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool up = tmax[r] > m_ref[r] + kRescaleTau;
+        const float m_new = up ? tmax[r] : m_ref[r];
+        const float alpha = up ? exp2_fast(m_ref[r] - m_new) : 1.f;
+        l_part[r] *= alpha;
+        m_ref[r] = m_new;
+        if (sn == 0) a_lds[wave][4 * sg + r] = alpha;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float alpha = a_lds[wave][4 * sg + r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[r][e] *= alpha;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    {
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mb = m_ref[r] == -INFINITY ? 0.f : m_ref[r];
+        pv[r] = exp2_fast(fmaf(sacc[r], c, -mb));
+        l_part[r] += pv[r];
+      }
+      *reinterpret_cast<f32x4*>(&p_lds[wave][sn][4 * sg]) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---- O += P V on the VALU (fp32) -------------------------------------
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const f32x4 pr = *reinterpret_cast<const f32x4*>(&p_lds[wave][i][4 * sg]);
+      float vf[8];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        vf[2 * e2] = bf16lo(vr[i][e2]);
+        vf[2 * e2 + 1] = bf16hi(vr[i][e2]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[r][e] = fmaf(pr[r], vf[e], oacc[r][e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- per-wave totals, then the merge of the four waves -------------------
+#pragma unroll
+  for (int r = 0; r < 4; ++r) l_part[r] = row16_sum(l_part[r]);
+  if (sn == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m_lds[wave][4 * sg + r] = m_ref[r];
+      l_lds[wave][4 * sg + r] = l_part[r];
+    }
+  }
+  {
+    float* op = o_part(wave);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<f32x4*>(op + (4 * sg + r) * D + 8 * dc) =
+          f32x4{oacc[r][0], oacc[r][1], oacc[r][2], oacc[r][3]};
+      *reinterpret_cast<f32x4*>(op + (4 * sg + r) * D + 8 * dc + 4) =
+          f32x4{oacc[r][4], oacc[r][5], oacc[r][6], oacc[r][7]};
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 16 * D; idx += kDecodeThreads) {
+    const int r = idx / D, d = idx % D;
+    if ((r & 3) >= G) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, m_lds[w][r]);
+    float lsum = 0.f, osum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = m_lds[w][r] == -INFINITY ? 0.f : exp2_fast(m_lds[w][r] - M);
+      lsum += f * l_lds[w][r];
+      osum += f * o_part(w)[r * D + d];
+    }
+    const int qh = (quad * NH + (r >> 2)) * G + (r & 3);
+    const int64_t slot = ((int64_t)b * p.Hq + qh) * p.max_splits + s;
+    p.part_o[slot * D + d] = osum / lsum;
+    if (d == 0) p.part_lse[slot] = M + log2_fast(lsum);
+  }
+}
+
 // One wave per (request, query head).  Lanes first take one split each to find
 // the largest partial LSE and the total weight; then every lane owns d/64
 // output columns and sums the weighted partials with all loads of a group of
@@ -394,12 +619,26 @@ static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
   }
 }
 
+// the four-head kernel's preconditions (its 16-token chunks start at multiples
+// of 16 and must not cross a page)
+static bool quad_ok(const DecodeParams& p) {
+  return p.group <= 4 && p.sub_groups == 1 && p.Hkv % kQuadHeads == 0 && p.page_size % 16 == 0 &&
+         p.split_tokens % 16 == 0;
+}
+
 template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p, int rows, hipStream_t stream) {
   // an empty plan (every request has length 0): the merge alone writes O = 0
   if (!p.planned || p.num_items > 0) {
-    if (p.page_size % 16 == 0) launch_split<D, true>(p, rows, stream);
-    else launch_split<D, false>(p, rows, stream);
+    if (D == 128 && quad_ok(p)) {
+      const int nq = p.Hkv / kQuadHeads;
+      const dim3 grid = p.planned ? dim3(p.num_items * nq) : dim3(nq, p.max_splits, p.B);
+      hipLaunchKernelGGL(decode_split_quad_kernel, grid, dim3(kDecodeThreads), 0, stream, p);
+    } else if (p.page_size % 16 == 0) {
+      launch_split<D, true>(p, rows, stream);
+    } else {
+      launch_split<D, false>(p, rows, stream);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -157,6 +157,11 @@ DECODE_CASES = [
     ([700, 129], 32, 2, 128, 32, 256, -1),         # 16 heads per KV head: two 8-row groups
     ([1000, 50], 6, 2, 64, 16, 512, 100),          # 3 heads per KV head, window
     ([0, 40], 4, 2, 128, 16, 512, -1),             # an empty cache
+    # four KV heads per workgroup (d = 128, <= 4 heads per KV head, 16 | page_size)
+    ([1, 15, 16, 17, 511, 512, 513, 1000], 32, 8, 128, 16, 512, -1),
+    ([700, 33, 129], 8, 8, 128, 16, 64, -1),       # MHA: one query per KV head
+    ([1000, 50, 3], 12, 4, 128, 32, 256, 100),     # 3 heads per KV head, window
+    ([517, 0, 77], 8, 4, 128, 16, 16, 37),         # 2 heads per KV head, 16-token splits
 ]
 
 
