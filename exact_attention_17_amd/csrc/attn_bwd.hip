@@ -234,6 +234,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     const uint32_t off = key < Lk ? (uint32_t)((int64_t)key * p.k_tok_stride + 8 * hi) * 2u : kOob;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) rf[t] = buf_load16(rr, off + 32u * t);
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) await_value(rf[t]);   // not inside the loop
   }
 
   // ---- query rows that see any key of the workgroup -----------------------
@@ -342,71 +344,129 @@ void bwd_dkdv_kernel(BwdParams p) {
   for (int db = 0; db < DBLK; ++db) acc[db] = f32x16{};
   const float c = p.scale_log2;
 
+  // S = Q K^T (role 0) or dP = dO V^T (role 1) of the tile's 32-row half qh.
+  // Lane (key n, half hi) holds rows 32qh + 8j + 4hi + e of the tile in
+  // element 4j + e.
+  auto product = [&](const char* rt, int qh) {
+    f32x16 S = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) S = mfma32x32x16(row_frag(rt, qh, t), rf[t], S);
+    return S;
+  };
+  // Role 0: P = 2^(S c - lse2), masked to the rows that see the lane's key
+  // (offsets rlo .. rlo + rcount - 1 from row 4hi of the tile); written to the
+  // partner as fp32 and packed as the bf16 B operand of dV^T += dO^T P.
+  auto make_p = [&](auto masked, const f32x16& S, const float* st, int qh, int rlo,
+                    uint32_t rcount, u32x4 (&ops)[2]) {
+    float (*xs)[64][4] = x_lds[qh][blk];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + 32 * qh + 8 * j + 4 * hi);
+      f32x4 pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pe = exp2_fast(fmaf(S[4 * j + e], c, -l2[e]));
+        if constexpr (decltype(masked)::value) {
+          const uint32_t off = (uint32_t)(32 * qh + 8 * j + e);
+          pe = (off - (uint32_t)rlo) < rcount ? pe : 0.f;
+        }
+        pv[e] = pe;
+      }
+      *reinterpret_cast<f32x4*>(xs[j][lane]) = pv;
+      ops[j >> 1][2 * (j & 1)] = pack_bf16x2(pv[0], pv[1]);
+      ops[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(pv[2], pv[3]);
+    }
+  };
+  // Role 1: dS = P (dP - delta), with P from the partner and dP in S.
+  auto make_ds = [&](const f32x16& S, const float* st, int qh, u32x4 (&ops)[2]) {
+    float (*xs)[64][4] = x_lds[qh][blk];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 dl = *reinterpret_cast<const f32x4*>(st + 64 + 32 * qh + 8 * j + 4 * hi);
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(xs[j][lane]);
+      float dv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dv[e] = pv[e] * (S[4 * j + e] - dl[e]);
+      ops[j >> 1][2 * (j & 1)] = pack_bf16x2(dv[0], dv[1]);
+      ops[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(dv[2], dv[3]);
+    }
+  };
+  // role 0: dV^T += dO^T P; role 1: dK^T += Q^T dS, for half qh
+  auto grad = [&](const char* tt, int qh, const u32x4 (&ops)[2]) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+        acc[db] = mfma32x32x16(tr_frag(tt, 2 * qh + c2, db), ops[c2], acc[db]);
+    }
+  };
+  // Order of a role-0 block: each MFMA, then a few VALU ops of the P
+  // computation and the next LDS read, so the exponentials run under the
+  // matrix core.
+  auto interleave = [](auto n_mfma) {
+#pragma unroll
+    for (int i = 0; i < decltype(n_mfma)::value; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+
   // One step: the 64-row tile s (in buffer `cur`) against the pair's 32 keys,
-  // as two 32-row halves.  Lane (key n, half hi) holds rows 32qh + 8j + 4hi + e
-  // of the tile in element 4j + e of S and dP.
+  // in three phases separated by barriers, so that each wave always has
+  // matrix work beside its vector work:
+  //   1. S, dP of both halves; role 0 forms P of half 0 under the MFMAs of half 1;
+  //   2. role 0: dV with P of half 0, forming P of half 1 under it;
+  //      role 1: dS of half 0 (P from the partner), dK with it;
+  //   3. dV with P of half 1; role 1: dS of half 1, dK with it.
   auto step = [&](auto parity, int s) {
     constexpr int cur = decltype(parity)::value;
     if (s + 1 < nsteps) fetch(s + 1, cur ^ 1);
     const int i0 = (qt_begin + s % nq) * 64;
     const int i_last = min(i0 + 63, Lq - 1);
     const bool full = key_lo(i_last) <= kw0 && key_hi(i0) >= kw0 + 32;
-    // offsets within the tile (from row i0 + 4hi) of the lane's visible rows:
-    // rlo .. rlo + rcount - 1 (rcount = 0 when no row sees the key)
     const int rlo = qmin_c - i0 - 4 * hi;
     const uint32_t rcount = (uint32_t)max(qmax_c - qmin_c + 1, 0);
     const char* rt = row_tiles + cur * TILE_BYTES;
     const char* tt = tr_tiles + cur * TILE_BYTES;
     const float* st = st_lds + cur * 256;
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      f32x16 S = f32x16{};
-#pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) S = mfma32x32x16(row_frag(rt, qh, t), rf[t], S);
-      float (*xs)[64][4] = x_lds[qh][blk];
-      u32x4 ops[2];
-      if (role == 0) {
-        // P = 2^(S c - lse2), masked; to the partner as fp32, to dV as bf16
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + 32 * qh + 8 * j + 4 * hi);
-          f32x4 pv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pe = exp2_fast(fmaf(S[4 * j + e], c, -l2[e]));
-            if (!full) {
-              const uint32_t off = (uint32_t)(32 * qh + 8 * j + e);
-              pe = (off - (uint32_t)rlo) < rcount ? pe : 0.f;
-            }
-            pv[e] = pe;
-          }
-          *reinterpret_cast<f32x4*>(xs[j][lane]) = pv;
-          ops[j >> 1][2 * (j & 1)] = pack_bf16x2(pv[0], pv[1]);
-          ops[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(pv[2], pv[3]);
-        }
+    using Masked = std::true_type;
+    using Full = std::false_type;
+    using Eight = std::integral_constant<int, 8>;
+    const f32x16 S0 = product(rt, 0);
+    f32x16 S1;
+    u32x4 ops0[2], ops1[2];
+    if (role == 0) {
+      if (full) {
+        S1 = product(rt, 1);
+        make_p(Full{}, S0, st, 0, rlo, rcount, ops0);
+        interleave(Eight{});
+      } else {
+        S1 = product(rt, 1);
+        make_p(Masked{}, S0, st, 0, rlo, rcount, ops0);
+        interleave(Eight{});
       }
-      __syncthreads();   // P of this half is in x_lds
-      if (role == 1) {
-        // dS = P (dP - delta), S holding dP here
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 dl = *reinterpret_cast<const f32x4*>(st + 64 + 32 * qh + 8 * j + 4 * hi);
-          const f32x4 pv = *reinterpret_cast<const f32x4*>(xs[j][lane]);
-          float dv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dv[e] = pv[e] * (S[4 * j + e] - dl[e]);
-          ops[j >> 1][2 * (j & 1)] = pack_bf16x2(dv[0], dv[1]);
-          ops[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(dv[2], dv[3]);
-        }
-      }
-      // role 0: dV^T += dO^T P; role 1: dK^T += Q^T dS
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-          acc[db] = mfma32x32x16(tr_frag(tt, 2 * qh + c2, db), ops[c2], acc[db]);
-      }
+    } else {
+      S1 = product(rt, 1);
     }
+    __syncthreads();   // P of half 0 is in x_lds
+    if (role == 0) {
+      if (full) {
+        grad(tt, 0, ops0);
+        make_p(Full{}, S1, st, 1, rlo, rcount, ops1);
+        interleave(Eight{});
+      } else {
+        grad(tt, 0, ops0);
+        make_p(Masked{}, S1, st, 1, rlo, rcount, ops1);
+        interleave(Eight{});
+      }
+    } else {
+      make_ds(S0, st, 0, ops0);
+      grad(tt, 0, ops0);
+    }
+    __syncthreads();   // P of half 1 is in x_lds
+    if (role == 1) make_ds(S1, st, 1, ops1);
+    grad(tt, 1, ops1);
     lds_load_wait();
     __syncthreads();
   };
@@ -500,6 +560,15 @@ void bwd_dq_kernel(BwdParams p) {
   // the tile's rows lie in the sequence's padded statistics
   const int64_t so = stat_offset(stat_base<VARLEN>(p, w.b, w.h, VARLEN ? w.q_base / kBlockM + w.b : 0) + row);
   const float lse2 = p.stat[so], dlt = p.stat[so + kBwdStatRows];
+  // all ordinary loads complete before the loop, whose direct-to-LDS loads
+  // the compiler's waits would otherwise count
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) {
+    await_value(qf[t]);
+    await_value(dof[t]);
+  }
+  await_value(lse2);
+  await_value(dlt);
 
   // ---- staging of K/V tiles (as in the forward, one swizzle for both) -----
   const uint32_t k_row_bytes = (uint32_t)(p.k_tok_stride * 2);

@@ -113,6 +113,13 @@ FA_DEV void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soff
 }
 FA_DEV void lds_load_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Forces the wait for a value from an ordinary (compiler-tracked) load at
+// this point.  A loop that also issues direct-to-LDS loads, which the compiler
+// does not see, must not inherit the wait for such a value: the vmcnt it
+// would place in the loop counts the invisible loads too and stalls on them.
+template <class T>
+FA_DEV void await_value(const T& v) { asm volatile("" ::"v"(v)); }
+
 FA_DEV bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Raw buffer resource over [base, base + bytes).  A load whose byte offset is
