@@ -473,23 +473,38 @@ void prefill_fwd_kernel(PrefillParams p) {
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2 ------------
+  // O goes out through the K tiles, unused from here on (the last step's
+  // barrier ended their reads): each lane holds 4-element pieces of one row,
+  // which stored directly would touch 32 rows per instruction.  Every wave
+  // writes its own 32 rows into the staging area (16-byte chunk c of row r at
+  // c ^ (r % chunks per row)), reads them back as 16-byte chunks, and stores
+  // whole contiguous rows.
   const float lpart = l_a + l_b;
   const float lt = lpart + xor32(lpart);
-  if (row < Lq) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* orow = og + (int64_t)row * p.q_tok_stride;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  {
+    constexpr int RB = 2 * D;                 // bytes per O row
+    constexpr int ORPI = 1024 / RB;           // rows per 1 KB store instruction
+    char* stage = reinterpret_cast<char*>(k_lds);   // 128 rows of RB bytes
+    const int rl = 32 * wave + n;             // the lane's row within the tile
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = 32 * db + 8 * g + 4 * hi;
-        const u32x2 val = u32x2{pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
-                                pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d) = val;
+        const int c = 4 * db + g;             // chunk of d = 32db + 8g .. +7; this lane has half hi
+        *reinterpret_cast<u32x2*>(stage + rl * RB + ((c ^ (rl & (KCH - 1))) * 16) + 8 * hi) =
+            u32x2{pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
+                  pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
       }
     }
-    if (lseg && hi == 0) lseg[row] = lt > 0.f ? (m_ref + log2_fast(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 32 / ORPI; ++i) {
+      const int r = 32 * wave + i * ORPI + lane / KCH, cc = lane % KCH;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * RB + ((cc ^ (r & (KCH - 1))) * 16));
+      if (q0 + r < Lq) *reinterpret_cast<u32x4*>(og + (int64_t)(q0 + r) * p.q_tok_stride + 8 * cc) = val;
+    }
   }
+  if (row < Lq && lseg && hi == 0) lseg[row] = lt > 0.f ? (m_ref + log2_fast(lt)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int d, int mode, hipStream_t stream) {
