@@ -480,18 +480,32 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
 
   // ---- epilogue: role 0 writes dV = dV^T, role 1 dK = scale * dK^T --------
-  if (key < Lk) {
-    uint16_t* dst = (role == 0 ? p.dv : p.dk) + kv_off + (int64_t)key * p.k_tok_stride;
+  // Staged through the Q (dV) and dO (dK) tiles, unused from here on: each
+  // wave writes its 32 key rows there (16-byte chunk c of row r at
+  // c ^ (r % chunks per row)), reads them back as 16-byte chunks and stores
+  // whole contiguous rows.
+  {
+    constexpr int RB = 2 * D;                 // bytes per output row
+    constexpr int ORPI = 1024 / RB;           // rows per 1 KB store instruction
+    char* stage = reinterpret_cast<char*>(role == 0 ? q_lds : do_lds);   // 128 rows of RB bytes
+    uint16_t* out = (role == 0 ? p.dv : p.dk) + kv_off;
     const float f = role == 0 ? 1.f : p.scale;
+    const int rl = 32 * blk + n;              // the lane's key within the workgroup
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * db + 8 * gq + 4 * hi;
-        *reinterpret_cast<u32x2*>(dst + d) =
+        const int cidx = 4 * db + gq;         // chunk of d = 32db + 8gq .. +7; this lane has half hi
+        *reinterpret_cast<u32x2*>(stage + rl * RB + ((cidx ^ (rl & (KCH - 1))) * 16) + 8 * hi) =
             u32x2{pack_bf16x2(acc[db][4 * gq] * f, acc[db][4 * gq + 1] * f),
                   pack_bf16x2(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
       }
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / ORPI; ++i) {
+      const int r = 32 * blk + i * ORPI + lane / KCH, cc = lane % KCH;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * RB + ((cc ^ (r & (KCH - 1))) * 16));
+      if (k0 + r < Lk) *reinterpret_cast<u32x4*>(out + (int64_t)(k0 + r) * p.k_tok_stride + 8 * cc) = val;
     }
   }
 }
@@ -672,17 +686,29 @@ void bwd_dq_kernel(BwdParams p) {
   }
 
   // ---- epilogue: dQ = scale * dQ^T, row-major ------------------------------
-  if (row < Lq) {
-    uint16_t* drow = p.dq + q_off + (int64_t)row * p.q_tok_stride;
+  // Staged through the K tiles, unused from here on (the last step's barrier
+  // ended their reads), so that stores write whole contiguous rows, as in the
+  // forward kernel.
+  {
+    constexpr int RB = 2 * D;                 // bytes per dQ row
+    constexpr int ORPI = 1024 / RB;           // rows per 1 KB store instruction
+    char* stage = reinterpret_cast<char*>(k_lds);   // 128 rows of RB bytes
+    const int rl = 32 * wave + n;             // the lane's row within the tile
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * db + 8 * gq + 4 * hi;
-        *reinterpret_cast<u32x2*>(drow + d) =
+        const int cidx = 4 * db + gq;
+        *reinterpret_cast<u32x2*>(stage + rl * RB + ((cidx ^ (rl & (KCH - 1))) * 16) + 8 * hi) =
             u32x2{pack_bf16x2(dqa[db][4 * gq] * p.scale, dqa[db][4 * gq + 1] * p.scale),
                   pack_bf16x2(dqa[db][4 * gq + 2] * p.scale, dqa[db][4 * gq + 3] * p.scale)};
       }
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / ORPI; ++i) {
+      const int r = 32 * wave + i * ORPI + lane / KCH, cc = lane % KCH;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * RB + ((cc ^ (r & (KCH - 1))) * 16));
+      if (q0 + r < Lq) *reinterpret_cast<u32x4*>(p.dq + q_off + (int64_t)(q0 + r) * p.q_tok_stride + 8 * cc) = val;
     }
   }
 }
