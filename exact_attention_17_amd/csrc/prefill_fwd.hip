@@ -167,12 +167,7 @@ void prefill_fwd_kernel(PrefillParams p) {
   const uint32_t k_bytes = Lk > 0 ? (uint32_t)(((int64_t)(Lk - 1) * p.k_tok_stride + D) * 2) : 0u;
   const uint32_t k_row_bytes = (uint32_t)(p.k_tok_stride * 2);
   u32x4 qf[KSTEPS];
-  {
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qg, q_bytes);
-    const uint32_t off = row < Lq ? (uint32_t)(row * p.q_tok_stride + 8 * hi) * 2u : kOob;
-#pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) qf[t] = buf_load16(qr, off + 32u * t);
-  }
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qg, q_bytes);
 
   // ---- staging of K/V tiles: global -> LDS directly ------------------------
   // Load instruction i of wave w fills tile bytes [(4i + w) KB, +1 KB): rows
@@ -270,6 +265,7 @@ void prefill_fwd_kernel(PrefillParams p) {
   // (c/scale)*tanh((scale/c)*s), with tanh(y) = 1 - 2/(e^{2y} + 1); the ALiBi
   // bias -slope*|pos - key| of the logit is -(slope/scale)*|pos - key| on s.
   const float alibi_s = MODS && p.alibi ? p.alibi[(int64_t)w.b * p.alibi_bstride + w.h] * p.alibi_scale : 0.f;
+  await_value(alibi_s);   // not inside the loop, whose direct-to-LDS loads a wait there would count
   auto modify = [&](f32x16 (&S)[2], int kb) {
     if (!MODS) return;
     const float two_log2e = 2.f * 1.4426950408889634f * p.cap_in;
@@ -394,26 +390,43 @@ void prefill_fwd_kernel(PrefillParams p) {
   // ---- prologue: K(0), K(1) into LDS, V buffer 1 zeroed; S^T(0) -----------
   // (step 0 multiplies V buffer 1 by P = 0: it must hold finite values)
   const int kb0 = kt_begin * kBlockN;
+  {
+    // the Q tile (128 rows) into the two V buffers, K swizzle
+    const uint32_t q_row_bytes = (uint32_t)(p.q_tok_stride * 2);
+    const int r = wave * RPI + lane / KCH;
+    const uint32_t q_src = (uint32_t)r * q_row_bytes + (uint32_t)(((lane % KCH) ^ Lds<D>::kswz(r)) * 16);
+#pragma unroll
+    for (int i = 0; i < 2 * LOADS; ++i) {
+      const uint32_t soff = (uint32_t)(q0 + 4 * i * RPI) * q_row_bytes;
+      lds_load16(qrs, q_src, (uint32_t)__builtin_amdgcn_readfirstlane(soff), v_lds_addr + wave_lds + 4096u * i);
+    }
+  }
   if (ntiles > 0) {
     const PageIds i0 = page_ids(kb0), i1 = page_ids(kb0 + kBlockN);
     fetch(krs, k_src, k_src_pg, kg, k_lds_addr, kb0, i0);
     if (ntiles > 1) fetch(krs, k_src, k_src_pg, kg, k_lds_addr + TILE_BYTES, kb0 + kBlockN, i1);
   }
-#pragma unroll
-  for (int i = 0; i < TILE_BYTES / 16 / kPrefillThreads; ++i)
-    reinterpret_cast<u32x4*>(v_lds + Lds<D>::kTile)[tid + i * kPrefillThreads] = u32x4{0u, 0u, 0u, 0u};
   lds_load_wait();
   __syncthreads();
+  {
+    const int rl = 32 * wave + n;
+    const char* qt = reinterpret_cast<const char*>(v_lds) + rl * 2 * D;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t)
+      qf[t] = *reinterpret_cast<const u32x4*>(qt + (((2 * t + hi) ^ Lds<D>::kswz(rl)) * 16));
+  }
   f32x16 s0[2], s1[2];
   u32x4 p0[4], p1[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p1[i] = u32x4{0u, 0u, 0u, 0u};
-  // Unconditional, so the Q loads are awaited here on every path: the compiler
-  // does not see the direct-to-LDS loads, and a Q wait left pending into the
-  // loop would be counted against them there.
   qk(0, s0);
-  // step 0 loads K(2) into K buffer 0: every wave must be done reading K(0)
+  // step 0 loads K(2) into K buffer 0 and V(0) over Q: every wave must be done
+  // reading K(0) and its Q rows
   __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TILE_BYTES / 16 / kPrefillThreads; ++i)
+    reinterpret_cast<u32x4*>(v_lds + Lds<D>::kTile)[tid + i * kPrefillThreads] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();   // step 0 multiplies V buffer 1 (now zeros) by P = 0
 
   // ---- main loop: two tiles per trip, ping-pong S and P registers ---------
   // Step j: S^T(j) and P_{j-1} are ready.  K(j+2) and V(j) are loaded into the
