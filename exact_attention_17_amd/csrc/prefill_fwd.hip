@@ -363,7 +363,7 @@ void prefill_fwd_kernel(PrefillParams p) {
   // Instruction order of the step's main block: a few K fragment reads first,
   // then each MFMA followed by some softmax VALU ops and the next LDS reads,
   // so reads stay a few MFMAs ahead and the VALU work hides under the MFMAs.
-  auto interleave_hint = [] {
+  auto interleave_hint = [](auto with_pv) {
 #ifndef IL_UP
 #define IL_UP 3
 #define IL_V1 4
@@ -378,17 +378,18 @@ void prefill_fwd_kernel(PrefillParams p) {
       __builtin_amdgcn_sched_group_barrier(0x002, IL_V1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, IL_R1, 0);
     }
+    if constexpr (decltype(with_pv)::value) {
 #pragma unroll
-    for (int i = 0; i < 4 * DBLK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, IL_V2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, IL_R2, 0);
+      for (int i = 0; i < 4 * DBLK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, IL_V2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, IL_R2, 0);
+      }
     }
     __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
   };
 
-  // ---- prologue: K(0), K(1) into LDS, V buffer 1 zeroed; S^T(0) -----------
-  // (step 0 multiplies V buffer 1 by P = 0: it must hold finite values)
+  // ---- prologue: Q, K(0), K(1) into LDS; S^T(0) ----------------------------
   const int kb0 = kt_begin * kBlockN;
   {
     // the Q tile (128 rows) into the two V buffers, K swizzle
@@ -417,16 +418,10 @@ void prefill_fwd_kernel(PrefillParams p) {
   }
   f32x16 s0[2], s1[2];
   u32x4 p0[4], p1[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p1[i] = u32x4{0u, 0u, 0u, 0u};
   qk(0, s0);
   // step 0 loads K(2) into K buffer 0 and V(0) over Q: every wave must be done
   // reading K(0) and its Q rows
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < TILE_BYTES / 16 / kPrefillThreads; ++i)
-    reinterpret_cast<u32x4*>(v_lds + Lds<D>::kTile)[tid + i * kPrefillThreads] = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();   // step 0 multiplies V buffer 1 (now zeros) by P = 0
 
   // ---- main loop: two tiles per trip, ping-pong S and P registers ---------
   // Step j: S^T(j) and P_{j-1} are ready.  K(j+2) and V(j) are loaded into the
@@ -437,10 +432,12 @@ void prefill_fwd_kernel(PrefillParams p) {
   // it must be raised then, P_{j-1} V_{j-1} is added first, O is rescaled and
   // P_{j-1} cleared, so the block adds zeros.  Afterwards the max is taken
   // only when the tile shows a probability above 2^8 (rare).
+  // Step 0 has no P_{-1}: its block holds only S^T(1) and the softmax of tile 0.
   // (the parity of j, and so every LDS buffer offset, is a compile-time constant)
-  auto step = [&](auto parity, int j, f32x16 (&Scur)[2], f32x16 (&Snxt)[2],
+  auto step = [&](auto parity, auto first, int j, f32x16 (&Scur)[2], f32x16 (&Snxt)[2],
                   u32x4 (&Pprev)[4], u32x4 (&Pcur)[4]) {
     constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
+    constexpr bool FIRST = decltype(first)::value;   // no P_{j-1} V_{j-1} before tile 0
     const int kb = kb0 + j * kBlockN;
     modify(Scur, kb);
     mask_tile(Scur, kb);
@@ -450,9 +447,11 @@ void prefill_fwd_kernel(PrefillParams p) {
     const bool exact = wave_any(m_ref == -INFINITY);
     if (exact) {
       update_max(Scur, [&] {
-        pv(nxt, Pprev);
+        if constexpr (!FIRST) {
+          pv(nxt, Pprev);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Pprev[i] = u32x4{0u, 0u, 0u, 0u};
+          for (int i = 0; i < 4; ++i) Pprev[i] = u32x4{0u, 0u, 0u, 0u};
+        }
       });
     }
     const PageIds ik = page_ids(kb + 2 * kBlockN), iv = page_ids(kb);
@@ -460,9 +459,9 @@ void prefill_fwd_kernel(PrefillParams p) {
     fetch(vrs, v_src, v_src_pg, vg, v_lds_addr + cur * TILE_BYTES, kb, iv);
     const float la0 = l_a, lb0 = l_b;
     qk(nxt, Snxt);
-    pv(nxt, Pprev);
+    if constexpr (!FIRST) pv(nxt, Pprev);
     softmax(Scur, Pcur);
-    interleave_hint();
+    interleave_hint(std::integral_constant<bool, !FIRST>{});
     // this lane's share of the tile's row sum bounds each of its probabilities
     // (also catches inf/NaN): above 2^8, take back the tile, raise the max and
     // rescale (P_{j-1} V_{j-1} is already in O, relative to the old max), and
@@ -476,9 +475,12 @@ void prefill_fwd_kernel(PrefillParams p) {
     lds_load_wait();
     __syncthreads();
   };
-  for (int j = 0; j < ntiles; j += 2) {
-    step(std::integral_constant<int, 0>{}, j, s0, s1, p1, p0);
-    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1, s1, s0, p0, p1);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if (ntiles > 0) step(P0{}, std::true_type{}, 0, s0, s1, p1, p0);
+  for (int j = 1; j < ntiles; j += 2) {
+    step(P1{}, std::false_type{}, j, s1, s0, p0, p1);
+    if (j + 1 < ntiles) step(P0{}, std::false_type{}, j + 1, s0, s1, p1, p0);
   }
   // the last tile's P V
   if (ntiles > 0) {
