@@ -282,15 +282,18 @@ void prefill_fwd_kernel(PrefillParams p) {
         S[kh][r] = x;
       }
   };
-  // mask only on tiles that cut through some row's visible band
+  // mask only on tiles that cut through some row's visible band; key k is
+  // visible iff (unsigned)(k - my_lo) < my_hi - my_lo, one compare per score
+  const uint32_t my_span = (uint32_t)max(my_hi - my_lo, 0);
   auto mask_tile = [&](f32x16 (&S)[2], int kb) {
     if (kb >= wlo_last && kb + kBlockN <= whi_first) return;
+    const uint32_t base = (uint32_t)(kb + 4 * hi - my_lo);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kb + 32 * kh + 8 * (r >> 2) + 4 * hi + (r & 3);
-        S[kh][r] = (key >= my_lo && key < my_hi) ? S[kh][r] : -INFINITY;
+        const uint32_t off = (uint32_t)(32 * kh + 8 * (r >> 2) + (r & 3));
+        S[kh][r] = base + off < my_span ? S[kh][r] : -INFINITY;
       }
   };
   // P = 2^(S*c - m) as packed bf16 MFMA fragments; l sums the unrounded fp32
