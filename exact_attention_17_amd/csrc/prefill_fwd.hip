@@ -43,10 +43,15 @@
 //     division by l makes the result exact either way.
 //   * K/V tiles are double-buffered in LDS and filled by buffer loads that
 //     write LDS directly (no VGPR staging, no ds_write): the loads of K(j+2)
-//     and V(j+1) are issued at the start of tile j and awaited at its end.
+//     and V(j) are issued at the start of tile j and awaited at its end.  The
+//     Q tile arrives the same way (into the V buffers, before the first V
+//     tile) and each wave reads its fragments from there.
 //     Rows past a sequence end come back as zeros from the buffer range
 //     check.  16-byte chunks are XOR-swizzled within each row so the MFMA
 //     operand reads and the transpose reads avoid LDS bank conflicts.
+//   * O leaves through the idle K buffers: each wave writes its normalised
+//     rows there and stores whole 256-byte rows, instead of 8-byte pieces of
+//     32 rows per store instruction.
 //   * Workgroup order: when the KV-group count is a multiple of 8, all query
 //     heads of a KV group land on one XCD (blocks are dealt to the 8 XCDs
 //     round-robin), a few KV groups at a time so their K/V stays in that L2;
@@ -100,7 +105,6 @@ void prefill_fwd_kernel(PrefillParams p) {
   constexpr int RPI = 64 / KCH;                  // rows per 1 KB load instruction
   constexpr int LOADS = kBlockN / RPI / 4;       // load instructions per wave per tile
   constexpr int TILE_BYTES = Lds<D>::kTile * 2;
-  static_assert(TILE_BYTES % (16 * kPrefillThreads) == 0, "V tile zero fill");
 
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * Lds<D>::kTile];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2 * Lds<D>::kTile];
@@ -162,7 +166,8 @@ void prefill_fwd_kernel(PrefillParams p) {
   const int row = qw0 + n;
   const int my_lo = key_lo(row), my_hi = key_hi(row);
 
-  // ---- Q fragments (B operand), resident for the whole loop --------------
+  // ---- sizes of the Q, K, V buffers; Q fragments (B operand) stay in ------
+  // registers for the whole loop (the tile is staged through LDS below)
   const uint32_t q_bytes = (uint32_t)(((int64_t)(Lq - 1) * p.q_tok_stride + D) * 2);
   const uint32_t k_bytes = Lk > 0 ? (uint32_t)(((int64_t)(Lk - 1) * p.k_tok_stride + D) * 2) : 0u;
   const uint32_t k_row_bytes = (uint32_t)(p.k_tok_stride * 2);
