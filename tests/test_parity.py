@@ -64,9 +64,10 @@ def test_dense_sweep(fa, case):
     check(f"dense{case}", o, lse, O, LSE)
 
 
-def test_dense_rescale_stress(fa):
+@pytest.mark.parametrize("d", [64, 128])
+def test_dense_rescale_stress(fa, d):
     """Scores that rise along the keys force the running max up on every tile."""
-    B, L, H, d = 1, 512, 2, 128
+    B, L, H = 1, 512, 2
     w = workloads.random_dense(77, B, L, L, H, H, d, True)
     k = w.k.float()
     qdir = w.q.float()[:, -1:, :, :] / w.q.float()[:, -1:, :, :].norm(dim=-1, keepdim=True)
@@ -174,6 +175,42 @@ def test_decode_sweep(fa, case):
     o, lse = run_decode(fa, w)
     O, LSE = decode_ref(w)
     check(f"decode{case}", o, lse, O, LSE)
+
+
+@pytest.mark.parametrize("case", [
+    # lens, Hq, Hkv, d, page_size, split: four-head kernel, then the general one
+    ([3000, 700, 1500], 32, 8, 128, 16, 512),
+    ([3000, 700, 1500], 8, 2, 128, 16, 512),
+    ([2000, 333], 8, 2, 64, 8, 256),
+])
+def test_decode_rescale_stress(fa, case):
+    """K rows gain a component along the request's mean query that grows with
+    the position, so the running max rises chunk after chunk (the rescale
+    branch of the split kernels), planned and unplanned."""
+    lens, Hq, Hkv, d, ps, split = case
+    npages = sum(-(-l // ps) for l in lens) + 3
+    w = workloads.random_paged(500 + Hq + d, lens, Hq, Hkv, d, ps, npages, split)
+    G = Hq // Hkv
+    kc = w.k_cache.float()
+    for b, n in enumerate(lens):
+        q = w.q[b, 0].float().view(Hkv, G, d).mean(dim=1)            # (Hkv, d)
+        qdir = q / q.norm(dim=-1, keepdim=True)
+        for j in range(n):
+            kc[w.block_table[b, j // ps], j % ps] += (200.0 * j / n) * qdir
+    w.k_cache = kc.to(torch.bfloat16)
+    # the input does what it is for: within a split, some 16-key chunk's max
+    # score exceeds the split's first chunk's by more than 2^8 (log2 units)
+    b, n = 0, lens[0]
+    keys = torch.stack([w.k_cache[w.block_table[b, j // ps], j % ps].float() for j in range(n)])
+    s2 = torch.einsum("jgd,gxd->jgx", keys, w.q[b, 0].float().view(Hkv, G, d)) * (w.scale / math.log(2))
+    cmax = s2[: n // 16 * 16].reshape(n // 16, 16, -1).amax(dim=(1, 2))
+    per = split // 16
+    assert any((cmax[i + 1:i + per] - cmax[i]).max() > 8 for i in range(0, len(cmax) - per, per))
+    O, LSE = decode_ref(w)
+    o, lse = run_decode(fa, w)
+    check(f"decode rescale{case}", o, lse, O, LSE)
+    o2, lse2 = run_decode_planned(fa, w)
+    check(f"decode rescale planned{case}", o2, lse2, O, LSE)
 
 
 def run_decode_planned(fa, w, plan=None):
