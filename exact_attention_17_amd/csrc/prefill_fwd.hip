@@ -399,6 +399,8 @@ void prefill_fwd_kernel(PrefillParams p) {
 
   // ---- prologue: Q, K(0), K(1) into LDS; S^T(0) ----------------------------
   const int kb0 = kt_begin * kBlockN;
+  // page ids of step 0's loads (paged mode; read one step ahead from then on)
+  PageIds ids_k = page_ids(kb0 + 2 * kBlockN), ids_v = page_ids(kb0);
   {
     // the Q tile (128 rows) into the two V buffers, K swizzle
     const uint32_t q_row_bytes = (uint32_t)(p.q_tok_stride * 2);
@@ -462,9 +464,11 @@ void prefill_fwd_kernel(PrefillParams p) {
         }
       });
     }
-    const PageIds ik = page_ids(kb + 2 * kBlockN), iv = page_ids(kb);
-    if (j + 2 < ntiles) fetch(krs, k_src, k_src_pg, kg, k_lds_addr + cur * TILE_BYTES, kb + 2 * kBlockN, ik);
-    fetch(vrs, v_src, v_src_pg, vg, v_lds_addr + cur * TILE_BYTES, kb, iv);
+    // page ids of this step's loads were read one step ahead (paged mode)
+    if (j + 2 < ntiles) fetch(krs, k_src, k_src_pg, kg, k_lds_addr + cur * TILE_BYTES, kb + 2 * kBlockN, ids_k);
+    fetch(vrs, v_src, v_src_pg, vg, v_lds_addr + cur * TILE_BYTES, kb, ids_v);
+    ids_k = page_ids(kb + 3 * kBlockN);
+    ids_v = page_ids(kb + kBlockN);
     const float la0 = l_a, lb0 = l_b;
     qk(nxt, Snxt);
     if constexpr (!FIRST) pv(nxt, Pprev);
