@@ -334,11 +334,6 @@ void bwd_dkdv_kernel(BwdParams p) {
     const u32x2 hi2 = tr_read_b64(reinterpret_cast<const uint16_t*>(a + (tr_base[1] ^ (64u * db))));
     return u32x4{lo[0], lo[1], hi2[0], hi2[1]};
   };
-  // the role's row operand (Q for S, dO for dP) and transposed operand (dO^T
-  // for dV, Q^T for dK)
-  const char* row_tiles = reinterpret_cast<const char*>(role == 0 ? q_lds : do_lds);
-  const char* tr_tiles = reinterpret_cast<const char*>(role == 0 ? do_lds : q_lds);
-
   f32x16 acc[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) acc[db] = f32x16{};
@@ -419,65 +414,67 @@ void bwd_dkdv_kernel(BwdParams p) {
   //   2. role 0: dV with P of half 0, forming P of half 1 under it;
   //      role 1: dS of half 0 (P from the partner), dK with it;
   //   3. dV with P of half 1; role 1: dS of half 1, dK with it.
-  auto step = [&](auto parity, int s) {
+  // (the role, the buffer parity and whether the tile needs the mask are
+  // compile-time constants of each instance, so no accumulator has to be
+  // merged across a branch)
+  auto step = [&](auto parity, auto role_c, auto masked, int s, int i0) {
     constexpr int cur = decltype(parity)::value;
+    constexpr int ROLE = decltype(role_c)::value;
     if (s + 1 < nsteps) fetch(s + 1, cur ^ 1);
-    const int i0 = (qt_begin + s % nq) * 64;
-    const int i_last = min(i0 + 63, Lq - 1);
-    const bool full = key_lo(i_last) <= kw0 && key_hi(i0) >= kw0 + 32;
     const int rlo = qmin_c - i0 - 4 * hi;
     const uint32_t rcount = (uint32_t)max(qmax_c - qmin_c + 1, 0);
-    const char* rt = row_tiles + cur * TILE_BYTES;
-    const char* tt = tr_tiles + cur * TILE_BYTES;
+    const char* rt = reinterpret_cast<const char*>(ROLE == 0 ? q_lds : do_lds) + cur * TILE_BYTES;
+    const char* tt = reinterpret_cast<const char*>(ROLE == 0 ? do_lds : q_lds) + cur * TILE_BYTES;
     const float* st = st_lds + cur * 256;
-    using Masked = std::true_type;
-    using Full = std::false_type;
     using Eight = std::integral_constant<int, 8>;
     const f32x16 S0 = product(rt, 0);
-    f32x16 S1;
+    __builtin_amdgcn_sched_barrier(0);   // half 1's MFMAs go with P of half 0 (below)
     u32x4 ops0[2], ops1[2];
-    if (role == 0) {
-      if (full) {
-        S1 = product(rt, 1);
-        make_p(Full{}, S0, st, 0, rlo, rcount, ops0);
-        interleave(Eight{});
-      } else {
-        S1 = product(rt, 1);
-        make_p(Masked{}, S0, st, 0, rlo, rcount, ops0);
-        interleave(Eight{});
-      }
-    } else {
-      S1 = product(rt, 1);
+    const f32x16 S1 = product(rt, 1);
+    if constexpr (ROLE == 0) {
+      make_p(masked, S0, st, 0, rlo, rcount, ops0);
+      interleave(Eight{});
     }
     __syncthreads();   // P of half 0 is in x_lds
-    if (role == 0) {
-      if (full) {
-        grad(tt, 0, ops0);
-        make_p(Full{}, S1, st, 1, rlo, rcount, ops1);
-        interleave(Eight{});
-      } else {
-        grad(tt, 0, ops0);
-        make_p(Masked{}, S1, st, 1, rlo, rcount, ops1);
-        interleave(Eight{});
-      }
+    if constexpr (ROLE == 0) {
+      grad(tt, 0, ops0);
+      make_p(masked, S1, st, 1, rlo, rcount, ops1);
+      interleave(Eight{});
     } else {
       make_ds(S0, st, 0, ops0);
       grad(tt, 0, ops0);
     }
     __syncthreads();   // P of half 1 is in x_lds
-    if (role == 1) make_ds(S1, st, 1, ops1);
+    if constexpr (ROLE == 1) make_ds(S1, st, 1, ops1);
     grad(tt, 1, ops1);
     lds_load_wait();
     __syncthreads();
+  };
+  // one step of this wave's role; P needs the mask unless every row of the
+  // tile sees all 32 keys of the pair (the dS wave multiplies by P, already
+  // masked, so it needs no variant)
+  auto role_step = [&](auto parity, auto role_c, int s) {
+    const int i0 = (qt_begin + s % nq) * 64;
+    const int i_last = min(i0 + 63, Lq - 1);
+    const bool full = key_lo(i_last) <= kw0 && key_hi(i0) >= kw0 + 32;
+    if (decltype(role_c)::value == 0 && !full)
+      step(parity, role_c, std::true_type{}, s, i0);
+    else
+      step(parity, role_c, std::false_type{}, s, i0);
+  };
+  auto run = [&](auto role_c) {
+    for (int s = 0; s < nsteps; s += 2) {
+      role_step(std::integral_constant<int, 0>{}, role_c, s);
+      if (s + 1 < nsteps) role_step(std::integral_constant<int, 1>{}, role_c, s + 1);
+    }
   };
 
   if (nsteps > 0) fetch(0, 0);
   lds_load_wait();
   __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    step(std::integral_constant<int, 0>{}, s);
-    if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, s + 1);
-  }
+  // both roles pass the same barriers in the same order (three per step)
+  if (role == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 
   // ---- epilogue: role 0 writes dV = dV^T, role 1 dK = scale * dK^T --------
   // Staged through the Q (dV) and dO (dK) tiles, unused from here on: each
