@@ -155,10 +155,14 @@ void bwd_prep_kernel(BwdParams p) {
 // dP, takes P (fp32) from its partner through LDS, forms dS and accumulates
 // dK^T.  Each wave then holds one resident operand and one accumulator, and
 // the MFMA work of a block splits evenly between the pair.
+// At d = 64 the kernel is held to 128 VGPRs (four waves per SIMD), so two
+// workgroups share a CU (2 x 66 KB of LDS) and each hides the other's
+// barriers; at d = 128 it needs 234 and runs one workgroup per CU.
 constexpr int kDkdvThreads = 512;
 
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(kDkdvThreads, 1)
+__global__ __attribute__((amdgpu_flat_work_group_size(kDkdvThreads, kDkdvThreads),
+                          amdgpu_waves_per_eu(D == 64 ? 4 : 2)))
 void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KSTEPS = D / 16;                 // MFMA steps over d
   constexpr int DBLK = D / 32;                   // 32-row blocks of dK^T, dV^T
