@@ -24,11 +24,13 @@
 //     per-wave LDS buffer; P*V runs on the fp32 VALU with V read in fully
 //     coalesced 256-byte rows.  The four waves merge in LDS and write one
 //     partial (O_s normalised, LSE_s) per query head.
-//   * decode_split_quad (d = 128, at most four query heads per KV head, page
-//     sizes that are multiples of 16): one workgroup per (request, split, four
-//     adjacent KV heads), so every load instruction reads 1 KB of contiguous
-//     cache memory (one token's rows of the four heads) instead of 256-byte
-//     pieces of four slots; the general kernel above serves the other shapes.
+//   * decode_split_heads<NH> (d = 128, page sizes that are multiples of 16;
+//     NH = 4 for at most four query heads per KV head, NH = 2 for five to
+//     eight): one workgroup per (request, split, NH adjacent KV heads), so
+//     every load instruction reads whole NH-head segments of contiguous cache
+//     memory (1 KB: one token's rows of four heads, or two tokens' rows of
+//     two heads) instead of 256-byte pieces of separate slots; the general
+//     kernel above serves the other shapes.
 //   * decode_merge: one wave per (request, query head) combines the
 //     partials by their LSE and writes bf16 O and fp32 LSE.
 //   * Keys at or past a request's length (and before its window) never reach
@@ -333,25 +335,33 @@ void decode_split_kernel(DecodeParams p) {
   }
 }
 
-// Four KV heads per workgroup (d = 128, at most four query heads per KV head,
-// page_size a multiple of 16).  The cache holds a token's rows of all KV heads
-// side by side, so heads 4x..4x+3 of one token are 1 KB of contiguous memory:
-// each load instruction reads exactly that (lane l: 16 bytes of head l/16),
-// instead of four 256-byte rows of one head in four different slots.  A wave
-// takes 16-token chunks; the 16 tokens lie in one page, so their page id is
-// one scalar load.  Scores: the A operand holds the 16 query rows of the four
-// heads (row 4h + j is query j of KV head h, zero when j >= group), and one
-// v_mfma_f32_16x16x32_bf16 chain per KV head h multiplies them with that
-// head's K rows; lanes 16h..16h+15 keep the result, which is exactly head h's
-// rows there.  P*V on the VALU: lane (h, c) holds d = 8c..8c+7 of head h for
-// each token, so its 4 x 8 output values need no cross-lane sum.
-constexpr int kQuadHeads = 4;
+// NH KV heads per workgroup (d = 128, page_size a multiple of 16): NH = 4
+// for at most four query heads per KV head, NH = 2 for five to eight.  The
+// cache holds a token's rows of all KV heads side by side, so heads
+// NH*x..NH*x+NH-1 of one token are NH * 256 bytes of contiguous memory, and
+// each load instruction reads whole such segments (one token for NH = 4, two
+// for NH = 2; 16 bytes per lane) instead of 256-byte rows of one head in
+// separate slots.  A wave takes 16-token chunks; the 16 tokens lie in one
+// page, so their page id is one scalar load.  Scores: the A operand holds 16
+// query rows, GM = 16 / NH per KV head (row GM*h + j is query j of KV head h,
+// zero when j >= group), and one v_mfma_f32_16x16x32_bf16 chain per KV head h
+// multiplies them with that head's K rows; the lanes whose four result rows
+// belong to head h keep that chain's result.  P*V on the VALU: a lane holds
+// d = 8c..8c+7 of one KV head for the tokens it loaded, so it accumulates
+// GM x 8 outputs of that head with no cross-lane sum (NH = 2: the two tokens
+// of a load go to lanes l and l + 32, added once at the end).
 constexpr int kQuadChunk = 16;   // tokens per wave iteration
 
+template <int NH>
 __global__ __launch_bounds__(kDecodeThreads, 2)
-void decode_split_quad_kernel(DecodeParams p) {
-  constexpr int D = 128, NH = kQuadHeads, CH = kQuadChunk, KT = D / 32;
-  constexpr int SEG = NH * D;        // elements of a token's four-head segment (1 KB)
+void decode_split_heads_kernel(DecodeParams p) {
+  static_assert(NH == 4 || NH == 2, "four or two KV heads per workgroup");
+  constexpr int D = 128, CH = kQuadChunk, KT = D / 32;
+  constexpr int GM = 16 / NH;        // query rows per KV head (zero-padded)
+  constexpr int SEG = NH * D;        // elements of a token's NH-head segment
+  constexpr int LPT = SEG / 8;       // lanes per token in one load (16 bytes each)
+  constexpr int TPL = 64 / LPT;      // tokens per load instruction
+  constexpr int LPC = CH / TPL;      // load instructions per chunk and operand
   constexpr int KST = SEG + 8;       // padded row of the per-wave K staging tile
   static_assert(16 * D * 4 <= CH * KST * 2, "wave partial must fit its K tile");
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[4][CH * KST];
@@ -361,20 +371,20 @@ void decode_split_quad_kernel(DecodeParams p) {
   auto o_part = [&](int w_) { return reinterpret_cast<float*>(&k_lds[w_][0]); };   // [16][D]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // grid = (head quad, split, request), or 1-D over (plan item, head quad)
-  // with the quads of one item adjacent
-  const int nquads = p.Hkv / NH;
-  int s, b, quad;
+  // grid = (head set, split, request), or 1-D over (plan item, head set)
+  // with the head sets of one item adjacent
+  const int nsets = p.Hkv / NH;
+  int s, b, hs;
   if (p.planned) {
-    const int item = blockIdx.x / nquads;
-    quad = blockIdx.x - item * nquads;
+    const int item = blockIdx.x / nsets;
+    hs = blockIdx.x - item * nsets;
     const __attribute__((address_space(4))) int* pc =
         (const __attribute__((address_space(4))) int*)p.plan;
     b = pc[2 * item];
     s = pc[2 * item + 1];
     if (b < 0 || b >= p.B || s < 0 || s >= p.max_splits) return;   // not an item of this batch
   } else {
-    quad = blockIdx.x;
+    hs = blockIdx.x;
     s = blockIdx.y;
     b = blockIdx.z;
   }
@@ -389,30 +399,34 @@ void decode_split_quad_kernel(DecodeParams p) {
 
   const int* bt = p.block_table + (int64_t)b * p.max_blocks;
   const int64_t tok_stride = (int64_t)p.Hkv * D;    // elements between cache slots
-  const uint16_t* kcache = p.k_cache + (int64_t)quad * SEG + 8 * lane;
-  const uint16_t* vcache = p.v_cache + (int64_t)quad * SEG + 8 * lane;
+  // load layout: lane (token tl of the load, 16-byte piece el of the segment)
+  const int tl = lane / LPT, el = lane % LPT;
+  const uint16_t* kcache = p.k_cache + (int64_t)hs * SEG + 8 * el;
+  const uint16_t* vcache = p.v_cache + (int64_t)hs * SEG + 8 * el;
 
-  // A operand: lane row i = lane % 16 (KV head i/4, query i%4), d = 32t + 8*(lane/16)
+  // A operand: lane row i = lane % 16 (KV head i / GM, query i % GM), d = 32t + 8*(lane/16)
   u32x4 qa[KT];
   {
     const int qi = lane & 15, qg = lane >> 4;
-    const bool ok = (qi & 3) < G;
-    const int qh = (quad * NH + (qi >> 2)) * G + (qi & 3);
+    const bool ok = (qi % GM) < G;
+    const int qh = (hs * NH + qi / GM) * G + qi % GM;
     const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + qh) * D + 8 * qg;
 #pragma unroll
     for (int t = 0; t < KT; ++t)
       qa[t] = ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * t) : u32x4{0, 0, 0, 0};
   }
 
-  // S layout: lane (key n = lane%16, head g = lane/16) holds head g's rows 0..3.
-  // PV layout: lane (head g = lane/16, d chunk dc = lane%16).
-  const int sn = lane & 15, sg = lane >> 4, dc = lane & 15;
+  // S layout: lane (key n = lane%16, g = lane/16) holds rows 4g..4g+3, all of
+  // KV head 4g / GM.  PV layout: the load layout, i.e. KV head hv = el / 16
+  // (rows GM*hv..GM*hv+GM-1) and d chunk dc = el % 16.
+  const int sn = lane & 15, sg = lane >> 4;
+  const int hv = el / 16, dc = el % 16;
   float m_ref[4], l_part[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) { m_ref[r] = -INFINITY; l_part[r] = 0.f; }
-  float oacc[4][8];
+  float oacc[GM][8];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < GM; ++r)
 #pragma unroll
     for (int e = 0; e < 8; ++e) oacc[r][e] = 0.f;
 
@@ -427,22 +441,24 @@ void decode_split_quad_kernel(DecodeParams p) {
     // the chunk's 16 tokens share one page (kc and page_size are multiples
     // of 16); tokens outside [k_beg, k_end) are read but masked below
     const int pid = __builtin_amdgcn_readfirstlane(bt[kc / p.page_size]);
-    const int64_t slot0 = (int64_t)pid * p.page_size + kc % p.page_size;
-    u32x4 kr[CH], vr[CH];
+    const int64_t slot0 = (int64_t)pid * p.page_size + kc % p.page_size + tl;
+    u32x4 kr[LPC], vr[LPC];
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
-      kr[i] = *reinterpret_cast<const u32x4*>(kcache + (slot0 + i) * tok_stride);
+    for (int i = 0; i < LPC; ++i)
+      kr[i] = *reinterpret_cast<const u32x4*>(kcache + (slot0 + TPL * i) * tok_stride);
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
-      vr[i] = *reinterpret_cast<const u32x4*>(vcache + (slot0 + i) * tok_stride);
+    for (int i = 0; i < LPC; ++i)
+      vr[i] = *reinterpret_cast<const u32x4*>(vcache + (slot0 + TPL * i) * tok_stride);
     if (partial) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i)
-        if (!(kc + i >= k_beg && kc + i < k_end)) vr[i] = u32x4{0, 0, 0, 0};
+      for (int i = 0; i < LPC; ++i) {
+        const int key = kc + TPL * i + tl;
+        if (!(key >= k_beg && key < k_end)) vr[i] = u32x4{0, 0, 0, 0};
+      }
     }
     // K through the wave's LDS tile into the B operand order
 #pragma unroll
-    for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(kt + i * KST + 8 * lane) = kr[i];
+    for (int i = 0; i < LPC; ++i) *reinterpret_cast<u32x4*>(kt + (TPL * i + tl) * KST + 8 * el) = kr[i];
     __builtin_amdgcn_wave_barrier();
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -451,7 +467,7 @@ void decode_split_quad_kernel(DecodeParams p) {
 #pragma unroll
       for (int t = 0; t < KT; ++t)
         acc = mfma16x16x32(qa[t], *reinterpret_cast<const u32x4*>(kt + sn * KST + h * D + 32 * t + 8 * sg), acc);
-      if (sg == h) sacc = acc;
+      if ((4 * sg) / GM == h) sacc = acc;
     }
     __builtin_amdgcn_wave_barrier();
     if (partial && !(kc + sn >= k_beg && kc + sn < k_end))
@@ -476,8 +492,8 @@ void decode_split_quad_kernel(DecodeParams p) {
       }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float alpha = a_lds[wave][4 * sg + r];
+      for (int r = 0; r < GM; ++r) {
+        const float alpha = a_lds[wave][GM * hv + r];
 #pragma unroll
         for (int e = 0; e < 8; ++e) oacc[r][e] *= alpha;
       }
@@ -496,8 +512,14 @@ void decode_split_quad_kernel(DecodeParams p) {
     __builtin_amdgcn_wave_barrier();
     // ---- O += P V on the VALU (fp32) -------------------------------------
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const f32x4 pr = *reinterpret_cast<const f32x4*>(&p_lds[wave][i][4 * sg]);
+    for (int i = 0; i < LPC; ++i) {
+      float pr[GM];
+#pragma unroll
+      for (int r4 = 0; r4 < GM; r4 += 4) {
+        const f32x4 q4 = *reinterpret_cast<const f32x4*>(&p_lds[wave][TPL * i + tl][GM * hv + r4]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pr[r4 + k] = q4[k];
+      }
       float vf[8];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -505,11 +527,17 @@ void decode_split_quad_kernel(DecodeParams p) {
         vf[2 * e2 + 1] = bf16hi(vr[i][e2]);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < GM; ++r)
 #pragma unroll
         for (int e = 0; e < 8; ++e) oacc[r][e] = fmaf(pr[r], vf[e], oacc[r][e]);
     }
     __builtin_amdgcn_wave_barrier();
+  }
+  if constexpr (TPL == 2) {   // lanes l and l + 32 summed different tokens
+#pragma unroll
+    for (int r = 0; r < GM; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) oacc[r][e] += xor32(oacc[r][e]);
   }
 
   // ---- per-wave totals, then the merge of the four waves -------------------
@@ -522,20 +550,20 @@ void decode_split_quad_kernel(DecodeParams p) {
       l_lds[wave][4 * sg + r] = l_part[r];
     }
   }
-  {
+  if (tl == 0) {
     float* op = o_part(wave);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<f32x4*>(op + (4 * sg + r) * D + 8 * dc) =
+    for (int r = 0; r < GM; ++r) {
+      *reinterpret_cast<f32x4*>(op + (GM * hv + r) * D + 8 * dc) =
           f32x4{oacc[r][0], oacc[r][1], oacc[r][2], oacc[r][3]};
-      *reinterpret_cast<f32x4*>(op + (4 * sg + r) * D + 8 * dc + 4) =
+      *reinterpret_cast<f32x4*>(op + (GM * hv + r) * D + 8 * dc + 4) =
           f32x4{oacc[r][4], oacc[r][5], oacc[r][6], oacc[r][7]};
     }
   }
   __syncthreads();
   for (int idx = tid; idx < 16 * D; idx += kDecodeThreads) {
     const int r = idx / D, d = idx % D;
-    if ((r & 3) >= G) continue;
+    if ((r % GM) >= G) continue;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, m_lds[w][r]);
@@ -546,7 +574,7 @@ void decode_split_quad_kernel(DecodeParams p) {
       lsum += f * l_lds[w][r];
       osum += f * o_part(w)[r * D + d];
     }
-    const int qh = (quad * NH + (r >> 2)) * G + (r & 3);
+    const int qh = (hs * NH + r / GM) * G + r % GM;
     const int64_t slot = ((int64_t)b * p.Hq + qh) * p.max_splits + s;
     p.part_o[slot * D + d] = osum / lsum;
     if (d == 0) p.part_lse[slot] = M + log2_fast(lsum);
@@ -619,21 +647,26 @@ static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
   }
 }
 
-// the four-head kernel's preconditions (its 16-token chunks start at multiples
-// of 16 and must not cross a page)
-static bool quad_ok(const DecodeParams& p) {
-  return p.group <= 4 && p.sub_groups == 1 && p.Hkv % kQuadHeads == 0 && p.page_size % 16 == 0 &&
-         p.split_tokens % 16 == 0;
+// KV heads per workgroup of the head-set kernel, or 0 for the general one
+// (the head-set kernel's 16-token chunks start at multiples of 16 and must
+// not cross a page)
+static int head_set(const DecodeParams& p) {
+  if (p.sub_groups != 1 || p.page_size % 16 != 0 || p.split_tokens % 16 != 0) return 0;
+  if (p.group <= 4 && p.Hkv % 4 == 0) return 4;
+  if (p.group > 4 && p.group <= 8 && p.Hkv % 2 == 0) return 2;
+  return 0;
 }
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p, int rows, hipStream_t stream) {
   // an empty plan (every request has length 0): the merge alone writes O = 0
   if (!p.planned || p.num_items > 0) {
-    if (D == 128 && quad_ok(p)) {
-      const int nq = p.Hkv / kQuadHeads;
-      const dim3 grid = p.planned ? dim3(p.num_items * nq) : dim3(nq, p.max_splits, p.B);
-      hipLaunchKernelGGL(decode_split_quad_kernel, grid, dim3(kDecodeThreads), 0, stream, p);
+    const int nh = D == 128 ? head_set(p) : 0;
+    if (nh > 0) {
+      const int nsets = p.Hkv / nh;
+      const dim3 grid = p.planned ? dim3(p.num_items * nsets) : dim3(nsets, p.max_splits, p.B);
+      if (nh == 4) hipLaunchKernelGGL(decode_split_heads_kernel<4>, grid, dim3(kDecodeThreads), 0, stream, p);
+      else hipLaunchKernelGGL(decode_split_heads_kernel<2>, grid, dim3(kDecodeThreads), 0, stream, p);
     } else if (p.page_size % 16 == 0) {
       launch_split<D, true>(p, rows, stream);
     } else {

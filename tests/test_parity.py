@@ -163,6 +163,11 @@ DECODE_CASES = [
     ([700, 33, 129], 8, 8, 128, 16, 64, -1),       # MHA: one query per KV head
     ([1000, 50, 3], 12, 4, 128, 32, 256, 100),     # 3 heads per KV head, window
     ([517, 0, 77], 8, 4, 128, 16, 16, 37),         # 2 heads per KV head, 16-token splits
+    # two KV heads per workgroup (d = 128, 5 to 8 heads per KV head, 16 | page_size)
+    ([1, 15, 16, 17, 511, 512, 513, 1000], 16, 2, 128, 16, 512, -1),
+    ([1000, 50, 3], 12, 2, 128, 32, 256, 100),     # 6 heads per KV head, window
+    ([517, 0, 77, 33], 28, 4, 128, 16, 16, -1),    # 7 heads per KV head, 16-token splits
+    ([300, 7, 900], 8, 1, 128, 16, 128, -1),       # 8 heads, one KV head: general kernel
 ]
 
 
@@ -178,8 +183,9 @@ def test_decode_sweep(fa, case):
 
 
 @pytest.mark.parametrize("case", [
-    # lens, Hq, Hkv, d, page_size, split: four-head kernel, then the general one
+    # lens, Hq, Hkv, d, page_size, split: four- and two-head kernels, then the general one
     ([3000, 700, 1500], 32, 8, 128, 16, 512),
+    ([3000, 700, 1500], 64, 8, 128, 16, 512),
     ([3000, 700, 1500], 8, 2, 128, 16, 512),
     ([2000, 333], 8, 2, 64, 8, 256),
 ])
