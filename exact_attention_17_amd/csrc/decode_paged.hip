@@ -24,13 +24,12 @@
 //     per-wave LDS buffer; P*V runs on the fp32 VALU with V read in fully
 //     coalesced 256-byte rows.  The four waves merge in LDS and write one
 //     partial (O_s normalised, LSE_s) per query head.
-//   * decode_split_heads<NH> (d = 128, page sizes that are multiples of 16;
-//     NH = 4 for at most four query heads per KV head, NH = 2 for five to
-//     eight): one workgroup per (request, split, NH adjacent KV heads), so
-//     every load instruction reads whole NH-head segments of contiguous cache
-//     memory (1 KB: one token's rows of four heads, or two tokens' rows of
-//     two heads) instead of 256-byte pieces of separate slots; the general
-//     kernel above serves the other shapes.
+//   * decode_split_heads<D, NH> (page sizes that are multiples of 16; NH = 4
+//     for at most four query heads per KV head, NH = 2 for five to eight):
+//     one workgroup per (request, split, NH adjacent KV heads), so every load
+//     instruction reads 1 KB of whole NH-head segments of contiguous cache
+//     memory (one to four tokens' rows of the NH heads) instead of row pieces
+//     of separate slots; the general kernel above serves the other shapes.
 //   * decode_merge: one wave per (request, query head) combines the
 //     partials by their LSE and writes bf16 O and fp32 LSE.
 //   * Keys at or past a request's length (and before its window) never reach
@@ -335,28 +334,29 @@ void decode_split_kernel(DecodeParams p) {
   }
 }
 
-// NH KV heads per workgroup (d = 128, page_size a multiple of 16): NH = 4
-// for at most four query heads per KV head, NH = 2 for five to eight.  The
-// cache holds a token's rows of all KV heads side by side, so heads
-// NH*x..NH*x+NH-1 of one token are NH * 256 bytes of contiguous memory, and
-// each load instruction reads whole such segments (one token for NH = 4, two
-// for NH = 2; 16 bytes per lane) instead of 256-byte rows of one head in
-// separate slots.  A wave takes 16-token chunks; the 16 tokens lie in one
+// NH KV heads per workgroup (page_size a multiple of 16): NH = 4 for at most
+// four query heads per KV head, NH = 2 for five to eight.  The cache holds a
+// token's rows of all KV heads side by side, so heads NH*x..NH*x+NH-1 of one
+// token are NH * 2d bytes of contiguous memory, and each load instruction
+// reads 1 KB of whole such segments (TPL = 1, 2 or 4 tokens; 16 bytes per
+// lane) instead of rows of one head in separate slots.  A wave takes 16-token chunks; the 16 tokens lie in one
 // page, so their page id is one scalar load.  Scores: the A operand holds 16
 // query rows, GM = 16 / NH per KV head (row GM*h + j is query j of KV head h,
 // zero when j >= group), and one v_mfma_f32_16x16x32_bf16 chain per KV head h
 // multiplies them with that head's K rows; the lanes whose four result rows
 // belong to head h keep that chain's result.  P*V on the VALU: a lane holds
 // d = 8c..8c+7 of one KV head for the tokens it loaded, so it accumulates
-// GM x 8 outputs of that head with no cross-lane sum (NH = 2: the two tokens
-// of a load go to lanes l and l + 32, added once at the end).
+// GM x 8 outputs of that head with no cross-lane sum (TPL > 1: the tokens of
+// a load go to lanes l, l + 64/TPL, ..., added once at the end).
 constexpr int kQuadChunk = 16;   // tokens per wave iteration
 
-template <int NH>
+template <int D, int NH>
 __global__ __launch_bounds__(kDecodeThreads, 2)
 void decode_split_heads_kernel(DecodeParams p) {
   static_assert(NH == 4 || NH == 2, "four or two KV heads per workgroup");
-  constexpr int D = 128, CH = kQuadChunk, KT = D / 32;
+  static_assert(D == 128 || D == 64, "head dim");
+  constexpr int CH = kQuadChunk, KT = D / 32;
+  constexpr int DC = D / 8;          // 16-byte pieces of one head's row
   constexpr int GM = 16 / NH;        // query rows per KV head (zero-padded)
   constexpr int SEG = NH * D;        // elements of a token's NH-head segment
   constexpr int LPT = SEG / 8;       // lanes per token in one load (16 bytes each)
@@ -417,10 +417,10 @@ void decode_split_heads_kernel(DecodeParams p) {
   }
 
   // S layout: lane (key n = lane%16, g = lane/16) holds rows 4g..4g+3, all of
-  // KV head 4g / GM.  PV layout: the load layout, i.e. KV head hv = el / 16
-  // (rows GM*hv..GM*hv+GM-1) and d chunk dc = el % 16.
+  // KV head 4g / GM.  PV layout: the load layout, i.e. KV head hv = el / DC
+  // (rows GM*hv..GM*hv+GM-1) and d chunk dc = el % DC.
   const int sn = lane & 15, sg = lane >> 4;
-  const int hv = el / 16, dc = el % 16;
+  const int hv = el / DC, dc = el % DC;
   float m_ref[4], l_part[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) { m_ref[r] = -INFINITY; l_part[r] = 0.f; }
@@ -533,11 +533,18 @@ void decode_split_heads_kernel(DecodeParams p) {
     }
     __builtin_amdgcn_wave_barrier();
   }
-  if constexpr (TPL == 2) {   // lanes l and l + 32 summed different tokens
+  // lanes l, l + 64/TPL, ... summed different tokens of the same outputs
+  if constexpr (TPL >= 2) {
 #pragma unroll
     for (int r = 0; r < GM; ++r)
 #pragma unroll
       for (int e = 0; e < 8; ++e) oacc[r][e] += xor32(oacc[r][e]);
+  }
+  if constexpr (TPL == 4) {
+#pragma unroll
+    for (int r = 0; r < GM; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) oacc[r][e] += xor16(oacc[r][e]);
   }
 
   // ---- per-wave totals, then the merge of the four waves -------------------
@@ -661,12 +668,12 @@ template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p, int rows, hipStream_t stream) {
   // an empty plan (every request has length 0): the merge alone writes O = 0
   if (!p.planned || p.num_items > 0) {
-    const int nh = D == 128 ? head_set(p) : 0;
+    const int nh = head_set(p);
     if (nh > 0) {
       const int nsets = p.Hkv / nh;
       const dim3 grid = p.planned ? dim3(p.num_items * nsets) : dim3(nsets, p.max_splits, p.B);
-      if (nh == 4) hipLaunchKernelGGL(decode_split_heads_kernel<4>, grid, dim3(kDecodeThreads), 0, stream, p);
-      else hipLaunchKernelGGL(decode_split_heads_kernel<2>, grid, dim3(kDecodeThreads), 0, stream, p);
+      if (nh == 4) hipLaunchKernelGGL((decode_split_heads_kernel<D, 4>), grid, dim3(kDecodeThreads), 0, stream, p);
+      else hipLaunchKernelGGL((decode_split_heads_kernel<D, 2>), grid, dim3(kDecodeThreads), 0, stream, p);
     } else if (p.page_size % 16 == 0) {
       launch_split<D, true>(p, rows, stream);
     } else {

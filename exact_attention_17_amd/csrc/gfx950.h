@@ -55,6 +55,12 @@ FA_DEV float xor32(float x) {
                                                      __float_as_int(x)));
 }
 
+// Value from lane (lane ^ 16).
+FA_DEV float xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ 16) << 2,
+                                                     __float_as_int(x)));
+}
+
 // Butterfly max / sum over the 16 lanes of a DPP row (lanes 16k..16k+15).
 // row_ror rotates within the row, quad_perm swaps within 4-lane groups.
 template <int CTRL>

@@ -168,6 +168,10 @@ DECODE_CASES = [
     ([1000, 50, 3], 12, 2, 128, 32, 256, 100),     # 6 heads per KV head, window
     ([517, 0, 77, 33], 28, 4, 128, 16, 16, -1),    # 7 heads per KV head, 16-token splits
     ([300, 7, 900], 8, 1, 128, 16, 128, -1),       # 8 heads, one KV head: general kernel
+    # d = 64 head sets: two tokens per load (NH = 4), four tokens per load (NH = 2)
+    ([1, 15, 16, 17, 511, 512, 513, 1000], 16, 4, 64, 16, 512, -1),
+    ([700, 33, 129], 16, 2, 64, 32, 64, 100),      # 8 heads per KV head, window
+    ([517, 0, 77], 20, 4, 64, 16, 16, -1),         # 5 heads per KV head, 16-token splits
 ]
 
 
@@ -186,6 +190,8 @@ def test_decode_sweep(fa, case):
     # lens, Hq, Hkv, d, page_size, split: four- and two-head kernels, then the general one
     ([3000, 700, 1500], 32, 8, 128, 16, 512),
     ([3000, 700, 1500], 64, 8, 128, 16, 512),
+    ([3000, 700, 1500], 32, 8, 64, 16, 512),
+    ([3000, 700, 1500], 64, 8, 64, 16, 512),
     ([3000, 700, 1500], 8, 2, 128, 16, 512),
     ([2000, 333], 8, 2, 64, 8, 256),
 ])
