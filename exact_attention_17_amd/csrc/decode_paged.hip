@@ -25,7 +25,8 @@
 //     coalesced 256-byte rows.  The four waves merge in LDS and write one
 //     partial (O_s normalised, LSE_s) per query head.
 //   * decode_split_heads<D, NH> (page sizes that are multiples of 16; NH = 4
-//     for at most four query heads per KV head, NH = 2 for five to eight):
+//     for at most four query heads per KV head, NH = 2 for more, taken in
+//     subgroups of eight):
 //     one workgroup per (request, split, NH adjacent KV heads), so every load
 //     instruction reads 1 KB of whole NH-head segments of contiguous cache
 //     memory (one to four tokens' rows of the NH heads) instead of row pieces
@@ -335,7 +336,8 @@ void decode_split_kernel(DecodeParams p) {
 }
 
 // NH KV heads per workgroup (page_size a multiple of 16): NH = 4 for at most
-// four query heads per KV head, NH = 2 for five to eight.  The cache holds a
+// four query heads per KV head, NH = 2 for more (eight per workgroup and KV
+// head; the rest in further subgroups that read the same keys).  The cache holds a
 // token's rows of all KV heads side by side, so heads NH*x..NH*x+NH-1 of one
 // token are NH * 2d bytes of contiguous memory, and each load instruction
 // reads 1 KB of whole such segments (TPL = 1, 2 or 4 tokens; 16 bytes per
@@ -371,23 +373,26 @@ void decode_split_heads_kernel(DecodeParams p) {
   auto o_part = [&](int w_) { return reinterpret_cast<float*>(&k_lds[w_][0]); };   // [16][D]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // grid = (head set, split, request), or 1-D over (plan item, head set)
-  // with the head sets of one item adjacent
-  const int nsets = p.Hkv / NH;
-  int s, b, hs;
+  // grid = (head set x query subgroup, split, request), or 1-D over (plan
+  // item, head set x query subgroup) with the workgroups of one item
+  // adjacent.  More than GM query heads per KV head (NH = 2 only): subgroup
+  // sub takes queries GM*sub..GM*sub+GM-1 of each KV head of the set.
+  const int per = (p.Hkv / NH) * p.sub_groups;
+  int s, b, hsub;
   if (p.planned) {
-    const int item = blockIdx.x / nsets;
-    hs = blockIdx.x - item * nsets;
+    const int item = blockIdx.x / per;
+    hsub = blockIdx.x - item * per;
     const __attribute__((address_space(4))) int* pc =
         (const __attribute__((address_space(4))) int*)p.plan;
     b = pc[2 * item];
     s = pc[2 * item + 1];
     if (b < 0 || b >= p.B || s < 0 || s >= p.max_splits) return;   // not an item of this batch
   } else {
-    hs = blockIdx.x;
+    hsub = blockIdx.x;
     s = blockIdx.y;
     b = blockIdx.z;
   }
+  const int hs = hsub / p.sub_groups, q0 = (hsub - hs * p.sub_groups) * GM;
   const int G = p.group;
 
   const int len = p.seqlens[b];
@@ -408,8 +413,8 @@ void decode_split_heads_kernel(DecodeParams p) {
   u32x4 qa[KT];
   {
     const int qi = lane & 15, qg = lane >> 4;
-    const bool ok = (qi % GM) < G;
-    const int qh = (hs * NH + qi / GM) * G + qi % GM;
+    const bool ok = q0 + qi % GM < G;
+    const int qh = (hs * NH + qi / GM) * G + q0 + qi % GM;
     const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + qh) * D + 8 * qg;
 #pragma unroll
     for (int t = 0; t < KT; ++t)
@@ -570,7 +575,7 @@ void decode_split_heads_kernel(DecodeParams p) {
   __syncthreads();
   for (int idx = tid; idx < 16 * D; idx += kDecodeThreads) {
     const int r = idx / D, d = idx % D;
-    if ((r % GM) >= G) continue;
+    if (q0 + r % GM >= G) continue;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, m_lds[w][r]);
@@ -581,7 +586,7 @@ void decode_split_heads_kernel(DecodeParams p) {
       lsum += f * l_lds[w][r];
       osum += f * o_part(w)[r * D + d];
     }
-    const int qh = (hs * NH + r / GM) * G + r % GM;
+    const int qh = (hs * NH + r / GM) * G + q0 + r % GM;
     const int64_t slot = ((int64_t)b * p.Hq + qh) * p.max_splits + s;
     p.part_o[slot * D + d] = osum / lsum;
     if (d == 0) p.part_lse[slot] = M + log2_fast(lsum);
@@ -657,10 +662,12 @@ static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
 // KV heads per workgroup of the head-set kernel, or 0 for the general one
 // (the head-set kernel's 16-token chunks start at multiples of 16 and must
 // not cross a page)
+// (more than 8 query heads per KV head: NH = 2 with subgroups of 8, the
+// host's head subgroups)
 static int head_set(const DecodeParams& p) {
-  if (p.sub_groups != 1 || p.page_size % 16 != 0 || p.split_tokens % 16 != 0) return 0;
+  if (p.page_size % 16 != 0 || p.split_tokens % 16 != 0) return 0;
   if (p.group <= 4 && p.Hkv % 4 == 0) return 4;
-  if (p.group > 4 && p.group <= 8 && p.Hkv % 2 == 0) return 2;
+  if (p.group > 4 && p.Hkv % 2 == 0 && p.sub_groups == (p.group + 7) / 8) return 2;
   return 0;
 }
 
@@ -670,8 +677,8 @@ static hipError_t launch_decode_d(const DecodeParams& p, int rows, hipStream_t s
   if (!p.planned || p.num_items > 0) {
     const int nh = head_set(p);
     if (nh > 0) {
-      const int nsets = p.Hkv / nh;
-      const dim3 grid = p.planned ? dim3(p.num_items * nsets) : dim3(nsets, p.max_splits, p.B);
+      const int per = p.Hkv / nh * p.sub_groups;
+      const dim3 grid = p.planned ? dim3(p.num_items * per) : dim3(per, p.max_splits, p.B);
       if (nh == 4) hipLaunchKernelGGL((decode_split_heads_kernel<D, 4>), grid, dim3(kDecodeThreads), 0, stream, p);
       else hipLaunchKernelGGL((decode_split_heads_kernel<D, 2>), grid, dim3(kDecodeThreads), 0, stream, p);
     } else if (p.page_size % 16 == 0) {

@@ -155,7 +155,7 @@ DECODE_CASES = [
     ([300, 64, 900], 4, 4, 64, 16, 0, -1),
     ([300, 7, 900], 8, 1, 128, 8, 128, -1),        # MQA, page_size 8 (< 16)
     ([333, 1, 64], 4, 2, 128, 1, 64, -1),          # page_size 1
-    ([700, 129], 32, 2, 128, 32, 256, -1),         # 16 heads per KV head: two 8-row groups
+    ([700, 129], 32, 2, 128, 32, 256, -1),         # 16 heads per KV head: two subgroups of 8
     ([1000, 50], 6, 2, 64, 16, 512, 100),          # 3 heads per KV head, window
     ([0, 40], 4, 2, 128, 16, 512, -1),             # an empty cache
     # four KV heads per workgroup (d = 128, <= 4 heads per KV head, 16 | page_size)
@@ -172,6 +172,9 @@ DECODE_CASES = [
     ([1, 15, 16, 17, 511, 512, 513, 1000], 16, 4, 64, 16, 512, -1),
     ([700, 33, 129], 16, 2, 64, 32, 64, 100),      # 8 heads per KV head, window
     ([517, 0, 77], 20, 4, 64, 16, 16, -1),         # 5 heads per KV head, 16-token splits
+    # more than 8 heads per KV head: two-head sets in query subgroups of 8
+    ([1000, 50, 3], 48, 4, 64, 16, 512, 100),      # 12 heads per KV head (4 in the last subgroup)
+    ([300, 7, 900], 16, 1, 128, 16, 128, -1),      # 16 heads, one KV head: general kernel
 ]
 
 
@@ -192,6 +195,7 @@ def test_decode_sweep(fa, case):
     ([3000, 700, 1500], 64, 8, 128, 16, 512),
     ([3000, 700, 1500], 32, 8, 64, 16, 512),
     ([3000, 700, 1500], 64, 8, 64, 16, 512),
+    ([3000, 700, 1500], 128, 8, 128, 16, 512),
     ([3000, 700, 1500], 8, 2, 128, 16, 512),
     ([2000, 333], 8, 2, 64, 8, 256),
 ])
