@@ -155,6 +155,8 @@ DECODE_CASES = [
     ([300, 64, 900], 4, 4, 64, 16, 0, -1),
     ([300, 7, 900], 8, 1, 128, 8, 128, -1),        # MQA, page_size 8 (< 16)
     ([333, 1, 64], 4, 2, 128, 1, 64, -1),          # page_size 1
+    ([300, 7, 900], 16, 2, 128, 8, 128, -1),       # general kernel, 8-row subgroups
+    ([1000, 50], 16, 2, 64, 8, 256, 300),          # the same at d = 64, window
     ([700, 129], 32, 2, 128, 32, 256, -1),         # 16 heads per KV head: two subgroups of 8
     ([1000, 50], 6, 2, 64, 16, 512, 100),          # 3 heads per KV head, window
     ([0, 40], 4, 2, 128, 16, 512, -1),             # an empty cache
@@ -173,8 +175,12 @@ DECODE_CASES = [
     ([700, 33, 129], 16, 2, 64, 32, 64, 100),      # 8 heads per KV head, window
     ([517, 0, 77], 20, 4, 64, 16, 16, -1),         # 5 heads per KV head, 16-token splits
     # more than 8 heads per KV head: two-head sets in query subgroups of 8
-    ([1000, 50, 3], 48, 4, 64, 16, 512, 100),      # 12 heads per KV head (4 in the last subgroup)
-    ([300, 7, 900], 16, 1, 128, 16, 128, -1),      # 16 heads, one KV head: general kernel
+    ([1000, 50, 3], 48, 4, 64, 16, 512, 100),      # 12 heads per KV head (4 in the last)
+    ([700, 33, 129], 40, 2, 128, 16, 256, -1),     # 20 heads per KV head: three subgroups
+    # odd Hkv: the general kernel (one scalar page id per 16-key block)
+    ([300, 7, 900], 16, 1, 128, 16, 128, -1),      # 16 heads, one KV head
+    ([517, 0, 77], 60, 3, 64, 32, 64, 200),        # 20 heads per KV head, window
+    ([700, 129], 12, 3, 128, 16, 512, -1),         # 4 heads per KV head, Hkv = 3
 ]
 
 
@@ -190,7 +196,8 @@ def test_decode_sweep(fa, case):
 
 
 @pytest.mark.parametrize("case", [
-    # lens, Hq, Hkv, d, page_size, split: four- and two-head kernels, then the general one
+    # lens, Hq, Hkv, d, page_size, split: head sets of four and two KV heads, then the
+    # general kernel (page size 8)
     ([3000, 700, 1500], 32, 8, 128, 16, 512),
     ([3000, 700, 1500], 64, 8, 128, 16, 512),
     ([3000, 700, 1500], 32, 8, 64, 16, 512),
