@@ -198,12 +198,15 @@ def gather_paged(cache, block_table_row, length, page_size):
 
 
 def decode_paged_ref(q, k_cache, v_cache, block_table, cache_seqlens, page_size,
-                     softmax_scale=None, window_left=-1):
+                     softmax_scale=None, window_left=-1, softcap=0.0, alibi_slopes=None):
     """One decode step over a paged KV cache ("flash-attention" skill page,
     appendix on PagedAttention / FlashDecoding; "FlashAttention-3 vs naive
     attention", sec. 2.2): each request's single query row attends to its
     cache_seqlens[b] cached tokens (all visible under bottom-right causal
-    alignment; a left window keeps the last window_left + 1).
+    alignment; a left window keeps the last window_left + 1).  softcap and
+    alibi_slopes ((Hq,) or (B, Hq)) are the score modifiers of attention_ref
+    (skill page sec. 3.3, with the kvcache call's arguments); the query sits
+    at position cache_seqlens[b] - 1.
 
     q: (B, 1, Hq, d); caches [num_pages, page_size, Hkv, d].  Returns
     O (B, 1, Hq, d) and LSE (B, Hq).
@@ -216,8 +219,12 @@ def decode_paged_ref(q, k_cache, v_cache, block_table, cache_seqlens, page_size,
         n = int(cache_seqlens[b])
         kk = _f64(gather_paged(k_cache, block_table[b], n, page_size))[None]
         vv = _f64(gather_paged(v_cache, block_table[b], n, page_size))[None]
+        sl = None
+        if alibi_slopes is not None:
+            a = np.asarray(alibi_slopes, dtype=np.float64)
+            sl = a if a.ndim == 1 else a[b]
         o, lse = attention_ref(q[b:b + 1], kk, vv, softmax_scale, causal=True,
-                               window=(window_left, -1))
+                               window=(window_left, -1), softcap=softcap, alibi_slopes=sl)
         O[b] = o[0]
         LSE[b] = lse[0, :, 0]
     return O, LSE

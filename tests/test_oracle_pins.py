@@ -637,6 +637,26 @@ def test_modifiers_varlen_and_kvcache_match_dense():
         assert np.abs(Okv[b] - Ob[0]).max() < 1e-12 and np.abs(LSEkv[b] - LSEb[0]).max() < 1e-12
 
 
+@pytest.mark.parametrize("window_left", [-1, 3])
+def test_modifiers_decode_match_brute_force(window_left):
+    # one query row per request at position len - 1 over a paged cache
+    rng = np.random.default_rng(34)
+    ps, lens = 4, [7, 1, 10]
+    perm = rng.permutation(8)
+    table = np.zeros((3, 3), dtype=np.int32)
+    table[0, :2], table[1, :1], table[2, :3] = perm[0:2], perm[2:3], perm[3:6]
+    kc, vc = rand(8, ps, 2, 3), rand(8, ps, 2, 3)
+    q = rand(3, 1, 4, 3)
+    slopes = rng.uniform(0.1, 0.6, (3, 4))
+    O, LSE = oracle.decode_paged_ref(q, kc, vc, table, lens, ps, 0.9, window_left, softcap=0.7,
+                                     alibi_slopes=slopes)
+    for b, n in enumerate(lens):
+        kk = oracle.gather_paged(kc, table[b], n, ps)[None]
+        vv = oracle.gather_paged(vc, table[b], n, ps)[None]
+        Ob, LSEb = brute_force_mod(q[b:b + 1], kk, vv, 0.9, True, window_left, -1, 0.7, slopes[b])
+        assert np.abs(O[b] - Ob[0]).max() < 1e-12 and np.abs(LSE[b] - LSEb[0, :, 0]).max() < 1e-12
+
+
 def test_modifier_planted_mistakes_are_caught(monkeypatch):
     orig_bias, orig_attend = oracle_attention.alibi_bias, oracle_attention.attend_rows
 
