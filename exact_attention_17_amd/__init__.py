@@ -56,12 +56,11 @@ _EXPORTS = {
                        + [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
     "fa_decode_paged_run": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int]
                             + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 7
-                            + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
-                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+                            + [ctypes.c_float, ctypes.c_int] + _MODS
+                            + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fa_decode_paged": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 2
-                        + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
-                                                ctypes.c_void_p, ctypes.c_size_t,
-                                                ctypes.c_void_p]),
+                        + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int] + _MODS
+                        + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fa_fwd_kvcache": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 8
                        + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int]
                        + _MODS + [ctypes.c_void_p]),
@@ -308,16 +307,19 @@ def _decode_args(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale,
 
 def fa_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale=None,
                     window_left=-1, split_tokens=0, out=None, lse=None, workspace=None,
-                    return_lse=True, stream=None):
+                    return_lse=True, stream=None, softcap=0.0, alibi_slopes=None):
     """Paged decode: q (B, 1, Hq, d), caches [num_pages, page_size, Hkv, d],
-    block_table int32 [B, max_blocks], cache_seqlens int32 [B] -> O, LSE (B, Hq)."""
+    block_table int32 [B, max_blocks], cache_seqlens int32 [B] -> O, LSE (B, Hq).
+    softcap / alibi_slopes ((Hq,) or (B, Hq) float32) as for fa_fwd; the query sits
+    at position cache_seqlens[b] - 1."""
     lib = load_library()
     out, lse, workspace, B, Hq, Hkv, d, num_pages, page_size, max_blocks, scale = _decode_args(
         q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, split_tokens, out, lse,
         workspace, return_lse)
     st = lib.fa_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                              _ptr(cache_seqlens), _ptr(out), _ptr(lse), B, Hq, Hkv, d, num_pages,
-                             page_size, max_blocks, scale, int(window_left), int(split_tokens),
+                             page_size, max_blocks, scale, int(window_left),
+                             *_mods(softcap, alibi_slopes, B, Hq), int(split_tokens),
                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(stream))
     _check("fa_decode_paged", st)
@@ -345,7 +347,8 @@ def fa_decode_plan(cache_seqlens, page_size, max_blocks_per_seq, window_left=-1,
 
 def fa_decode_paged_run(q, k_cache, v_cache, block_table, cache_seqlens, plan,
                         softmax_scale=None, window_left=-1, split_tokens=0, out=None, lse=None,
-                        workspace=None, return_lse=True, stream=None):
+                        workspace=None, return_lse=True, stream=None, softcap=0.0,
+                        alibi_slopes=None):
     """fa_decode_paged over the items of a plan from fa_decode_plan (same lengths, page size,
     block-table width, window and split size), uploaded as a device int32 tensor
     (num_items, 2)."""
@@ -360,7 +363,8 @@ def fa_decode_paged_run(q, k_cache, v_cache, block_table, cache_seqlens, plan,
     st = lib.fa_decode_paged_run(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                  _ptr(cache_seqlens), _ptr(plan), plan.shape[0], _ptr(out),
                                  _ptr(lse), B, Hq, Hkv, d, num_pages, page_size, max_blocks,
-                                 scale, int(window_left), int(split_tokens), _ptr(workspace),
+                                 scale, int(window_left), *_mods(softcap, alibi_slopes, B, Hq),
+                                 int(split_tokens), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check("fa_decode_paged_run", st)
     return out, lse

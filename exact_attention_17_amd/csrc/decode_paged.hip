@@ -49,6 +49,18 @@ namespace fa {
 namespace {
 constexpr float kRescaleTau = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2eF = 1.4426950408889634f;
+
+// Score modifiers on a raw dot product s = q.k, softcap then ALiBi, as in the
+// prefill kernel: the capped logit c * tanh(scale * s / c) is kept in
+// dot-product units as cap_out * tanh(cap_in * s), with tanh(y) = 1 - 2 /
+// (e^{2y} + 1), and ALiBi subtracts (slope / scale) * |query pos - key pos|
+// (slope already divided by the scale).
+__device__ __forceinline__ float modify_score(const DecodeParams& p, float s, float slope, int dist) {
+  if (p.cap_in > 0.f)
+    s = p.cap_out * (1.f - 2.f * __builtin_amdgcn_rcpf(exp2_fast(s * (2.f * kLog2eF * p.cap_in)) + 1.f));
+  return s - slope * (float)dist;
+}
 }  // namespace
 
 // GR = padded number of query heads handled per workgroup (1, 2, 4 or 8).
@@ -133,6 +145,15 @@ void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) oacc[r][e] = 0.f;
 
+  // score modifiers (the query sits at position len - 1); the slope of S row
+  // 4*sg + r (0 for padding rows) is read where it is used, so that nothing
+  // extra stays live through the loop
+  const bool mods = p.cap_in > 0.f || p.alibi != nullptr;
+  auto slope_of = [&](int r) {
+    return p.alibi && 4 * sg + r < nrow
+               ? p.alibi[(int64_t)b * p.alibi_bstride + h0 + 4 * sg + r] * p.alibi_scale : 0.f;
+  };
+
   const float c = p.scale_log2;
   const int nchunks = (k_end - split_base + kDecodeChunk - 1) / kDecodeChunk;
   const int c0 = (k_beg - split_base) / kDecodeChunk;
@@ -201,6 +222,10 @@ void decode_split_kernel(DecodeParams p) {
 #pragma unroll
       for (int t = 0; t < KT; ++t) sacc[blk] = mfma16x16x32(qa[t], kr[blk][t], sacc[blk]);
       const int key = kc + 16 * blk + sn;
+      if (mods) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[blk][r] = modify_score(p, sacc[blk][r], slope_of(r), abs(len - 1 - key));
+      }
       if (partial && !(key >= k_beg && key < k_end))
         sacc[blk] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
@@ -435,6 +460,17 @@ void decode_split_heads_kernel(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) oacc[r][e] = 0.f;
 
+  // score modifiers (the query sits at position len - 1); the slope of S row
+  // i = 4*sg + r (0 for padding rows) is read where it is used, so that
+  // nothing extra stays live through the loop
+  const bool mods = p.cap_in > 0.f || p.alibi != nullptr;
+  auto slope_of = [&](int r) {
+    const int i = 4 * sg + r;
+    return p.alibi && q0 + i % GM < G
+               ? p.alibi[(int64_t)b * p.alibi_bstride + (hs * NH + i / GM) * G + q0 + i % GM] * p.alibi_scale
+               : 0.f;
+  };
+
   const float c = p.scale_log2;
   const int nchunks = (k_end - split_base + CH - 1) / CH;
   const int c0 = (k_beg - split_base) / CH;
@@ -475,6 +511,10 @@ void decode_split_heads_kernel(DecodeParams p) {
       if ((4 * sg) / GM == h) sacc = acc;
     }
     __builtin_amdgcn_wave_barrier();
+    if (mods) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[r] = modify_score(p, sacc[r], slope_of(r), abs(len - 1 - (kc + sn)));
+    }
     if (partial && !(kc + sn >= k_beg && kc + sn < k_end))
       sacc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     // ---- online softmax per query row ------------------------------------

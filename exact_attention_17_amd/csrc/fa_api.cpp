@@ -316,10 +316,12 @@ fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                       const int* block_table, const int* cache_seqlens, bool planned,
                       const int* plan, int num_items, void* o, float* lse, int B, int Hq, int Hkv, int d,
                       int num_pages, int page_size, int max_blocks_per_seq,
-                      float softmax_scale, int window_left, int split_tokens,
+                      float softmax_scale, int window_left, float softcap,
+                      const float* alibi_slopes, int alibi_batch_stride, int split_tokens,
                       void* workspace, size_t workspace_bytes, void* stream) {
   fa_status st = check_common(Hq, Hkv, d, softmax_scale, 0, window_left, -1);
   if (st != FA_OK) return st;
+  if ((st = check_mods(softcap, alibi_slopes, alibi_batch_stride, Hq)) != FA_OK) return st;
   if ((st = check_tensors(q, k_cache, v_cache, o, lse)) != FA_OK) return st;
   if (!block_table || !cache_seqlens || !aligned(block_table, 4) || !aligned(cache_seqlens, 4))
     return FA_ERR_INVALID_ARG;
@@ -365,6 +367,11 @@ fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   p.planned = planned;
   p.plan = plan;
   p.num_items = num_items;
+  p.cap_in = softcap > 0.f ? softmax_scale / softcap : 0.f;
+  p.cap_out = softcap > 0.f ? softcap / softmax_scale : 0.f;
+  p.alibi = alibi_slopes;
+  p.alibi_bstride = alibi_slopes ? alibi_batch_stride : 0;
+  p.alibi_scale = 1.f / softmax_scale;
   hipError_t e = fa::launch_decode(p, d, rows, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -377,22 +384,27 @@ fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cach
                           const int* block_table, const int* cache_seqlens,
                           void* o, float* lse, int B, int Hq, int Hkv, int d,
                           int num_pages, int page_size, int max_blocks_per_seq,
-                          float softmax_scale, int window_left, int split_tokens,
+                          float softmax_scale, int window_left, float softcap,
+                          const float* alibi_slopes, int alibi_batch_stride, int split_tokens,
                           void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, block_table, cache_seqlens, false, nullptr, 0, o, lse, B, Hq,
                      Hkv, d, num_pages, page_size, max_blocks_per_seq, softmax_scale,
-                     window_left, split_tokens, workspace, workspace_bytes, stream);
+                     window_left, softcap, alibi_slopes, alibi_batch_stride, split_tokens,
+                     workspace, workspace_bytes, stream);
 }
 
 fa_status fa_decode_paged_run(const void* q, const void* k_cache, const void* v_cache,
                               const int* block_table, const int* cache_seqlens, const int* plan,
                               int num_items, void* o, float* lse, int B, int Hq, int Hkv, int d,
                               int num_pages, int page_size, int max_blocks_per_seq,
-                              float softmax_scale, int window_left, int split_tokens,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              float softmax_scale, int window_left, float softcap,
+                              const float* alibi_slopes, int alibi_batch_stride,
+                              int split_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   return decode_impl(q, k_cache, v_cache, block_table, cache_seqlens, true, plan, num_items, o, lse, B,
                      Hq, Hkv, d, num_pages, page_size, max_blocks_per_seq, softmax_scale,
-                     window_left, split_tokens, workspace, workspace_bytes, stream);
+                     window_left, softcap, alibi_slopes, alibi_batch_stride, split_tokens,
+                     workspace, workspace_bytes, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Lq) {

@@ -117,6 +117,11 @@ struct DecodeParams {
   bool planned;            // false: grid over every (split, request) slot
   const int* plan;         // planned: (request, split) pairs, one per item
   int num_items;
+  // score modifiers, as in PrefillParams (cap_in = 0 and alibi = NULL: off)
+  float cap_in, cap_out;
+  const float* alibi;
+  int alibi_bstride;
+  float alibi_scale;
 };
 
 // mode: 0 dense, 1 varlen, 2 paged KV cache

@@ -34,15 +34,16 @@
  *     the keys to [i + Lk - Lq - left, i + Lk - Lq + right] inclusive;
  *     -1 leaves that side unbounded.  A row with no visible key gets O = 0
  *     and LSE = -inf.
- *   - Score modifiers of the prefill entry points (fa_fwd, fa_fwd_varlen,
- *     fa_fwd_kvcache; skill page sec. 3.3): softcap > 0 replaces each logit
+ *   - Score modifiers of the attention entry points (fa_fwd, fa_fwd_varlen,
+ *     fa_fwd_kvcache, fa_decode_paged; skill page sec. 3.3): softcap > 0 replaces each logit
  *     x = softmax_scale * q.k by softcap * tanh(x / softcap) (0 = off; must
  *     be finite and >= 0).  alibi_slopes (device float32, or NULL = off) adds
  *     -slope * |i + Lk - Lq - j| to the logit of query row i and key j, after
  *     the softcap and before the mask; the slope of (batch b, query head h)
  *     is alibi_slopes[b * alibi_batch_stride + h], with alibi_batch_stride 0
  *     (slopes of shape (Hq,)) or Hq (shape (B, Hq); for varlen, b is the
- *     sequence index).  Paged decode takes neither.
+ *     sequence index).  In paged decode the one query row of request b sits
+ *     at position cache_seqlens[b] - 1.  The backward takes neither.
  *   - Errors: every argument is validated on the host before any HIP call.
  *     On a non-zero status nothing has been enqueued and no output has been
  *     touched.  FA_ERR_HIP reports a failed kernel launch.  Device-side
@@ -173,6 +174,7 @@ size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_blocks_per_s
  *       A request with len 0 gets O = 0, LSE = -inf.
  *   lse      : (B, Hq) float32, or NULL
  *   window_left : -1 for none, else only the last window_left + 1 tokens count.
+ *   softcap, alibi_slopes, alibi_batch_stride : the score modifiers above.
  *   split_tokens : 0 (= 512) or a positive multiple of 16.
  *   workspace : device buffer of at least fa_decode_paged_workspace_size(...)
  *       bytes, 256-byte aligned; its contents on entry do not matter.
@@ -183,7 +185,8 @@ fa_status fa_decode_paged(const void* q, const void* k_cache, const void* v_cach
                           const int* block_table, const int* cache_seqlens,
                           void* o, float* lse, int B, int Hq, int Hkv, int d,
                           int num_pages, int page_size, int max_blocks_per_seq,
-                          float softmax_scale, int window_left, int split_tokens,
+                          float softmax_scale, int window_left, float softcap,
+                          const float* alibi_slopes, int alibi_batch_stride, int split_tokens,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -228,8 +231,10 @@ fa_status fa_decode_paged_run(const void* q, const void* k_cache, const void* v_
                               const int* block_table, const int* cache_seqlens, const int* plan,
                               int num_items, void* o, float* lse, int B, int Hq, int Hkv, int d,
                               int num_pages, int page_size, int max_blocks_per_seq,
-                              float softmax_scale, int window_left, int split_tokens,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              float softmax_scale, int window_left, float softcap,
+                              const float* alibi_slopes, int alibi_batch_stride,
+                              int split_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * Attention of Lq new query tokens per request over a paged KV cache

@@ -2,6 +2,7 @@
 entry point include/fa.h declares, and rejects each invalid argument with its
 status code before any HIP call (so nothing is enqueued)."""
 
+import math
 import ctypes
 import os
 import re
@@ -139,11 +140,12 @@ def test_workspace_size(lib):
 
 def decode(lib, **kw):
     a = dict(q=P, kc=P, vc=P, bt=P, sl=P, o=P, lse=P, B=4, Hq=8, Hkv=2, d=128, pages=64, ps=16,
-             mb=8, scale=0.1, wl=-1, split=0, ws=P, wsb=1 << 30)
+             mb=8, scale=0.1, wl=-1, cap=0.0, al=None, ast=0, split=0, ws=P, wsb=1 << 30)
     a.update(kw)
     return lib.fa_decode_paged(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["o"], a["lse"], a["B"],
                                a["Hq"], a["Hkv"], a["d"], a["pages"], a["ps"], a["mb"], a["scale"],
-                               a["wl"], a["split"], a["ws"], a["wsb"], None)
+                               a["wl"], a["cap"], a["al"], a["ast"], a["split"], a["ws"], a["wsb"],
+                               None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -152,7 +154,8 @@ def decode(lib, **kw):
     (dict(split=24), INVALID), (dict(split=-16), INVALID), (dict(wl=-2), INVALID),
     (dict(Hkv=3), INVALID), (dict(d=32), UNSUPPORTED), (dict(scale=0.0), INVALID),
     (dict(ws=None), WORKSPACE), (dict(ws=P + 16), WORKSPACE), (dict(wsb=1024), WORKSPACE),
-    (dict(B=70000), INVALID),
+    (dict(B=70000), INVALID), (dict(cap=-1.0), INVALID), (dict(cap=math.inf), INVALID),
+    (dict(al=P + 2), INVALID), (dict(al=P, ast=3), INVALID),
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
@@ -160,12 +163,13 @@ def test_decode_rejects(lib, kw, code):
 
 def decode_run(lib, **kw):
     a = dict(q=P, kc=P, vc=P, bt=P, sl=P, plan=P, n=4, o=P, lse=P, B=4, Hq=8, Hkv=2, d=128,
-             pages=64, ps=16, mb=8, scale=0.1, wl=-1, split=0, ws=P, wsb=1 << 30)
+             pages=64, ps=16, mb=8, scale=0.1, wl=-1, cap=0.0, al=None, ast=0, split=0, ws=P,
+             wsb=1 << 30)
     a.update(kw)
     return lib.fa_decode_paged_run(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["plan"], a["n"],
                                    a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"],
-                                   a["pages"], a["ps"], a["mb"], a["scale"], a["wl"], a["split"],
-                                   a["ws"], a["wsb"], None)
+                                   a["pages"], a["ps"], a["mb"], a["scale"], a["wl"], a["cap"],
+                                   a["al"], a["ast"], a["split"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [

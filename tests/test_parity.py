@@ -514,3 +514,36 @@ def test_varlen_and_kvcache_score_modifiers(fa):
                                                 bits(kv.k_new), bits(kv.v_new), kv.scale, True,
                                                 softcap=20.0, alibi_slopes=sl)
     check("kvcache mods", o, lse, O, LSE)
+
+
+@pytest.mark.parametrize("case", [
+    # lens, Hq, Hkv, d, page_size, split, window_left, softcap, alibi
+    ([1000, 17, 513], 32, 8, 128, 16, 512, -1, 0.5, "none"),     # four-head sets
+    ([1000, 17, 513], 32, 8, 128, 16, 256, 300, 0.0, "head"),
+    ([700, 33, 129], 16, 2, 128, 32, 64, -1, 1.0, "batch"),      # two-head sets (8 per KV head)
+    ([700, 33, 129], 48, 4, 64, 16, 512, 100, 2.0, "head"),      # 12 per KV head, d = 64
+    ([300, 7, 900], 8, 2, 128, 8, 128, -1, 0.7, "batch"),        # general kernel (page size 8)
+    ([300, 7, 900], 16, 1, 64, 16, 128, 200, 0.0, "batch"),      # general kernel, one KV head
+])
+def test_decode_score_modifiers(fa, case):
+    """softcap and ALiBi in paged decode, unplanned and planned (the query at
+    position len - 1)."""
+    lens, Hq, Hkv, d, ps, split, wl, cap, al = case
+    npages = sum(-(-l // ps) for l in lens) + 3
+    w = workloads.random_paged(900 + Hq + d + ps, lens, Hq, Hkv, d, ps, npages, split,
+                               window_left=wl)
+    slopes = None if al == "none" else alibi_slopes(Hq, len(lens) if al == "batch" else None)
+    sl_dev = None if slopes is None else dev(torch.from_numpy(slopes))
+    O, LSE = oracle.decode_paged_ref(bits(w.q), bits(w.k_cache), bits(w.v_cache), w.block_table,
+                                     w.seqlens, w.page_size, w.scale, wl, softcap=cap,
+                                     alibi_slopes=slopes)
+    args = (dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(torch.from_numpy(w.block_table)),
+            dev(torch.from_numpy(w.seqlens)))
+    o, lse = fa.fa_decode_paged(*args, w.scale, wl, split, softcap=cap, alibi_slopes=sl_dev)
+    torch.cuda.synchronize()
+    check(f"decode mods{case}", o.cpu(), lse.cpu(), O, LSE)
+    plan = fa.fa_decode_plan(w.seqlens, ps, w.block_table.shape[1], wl, split)
+    o2, lse2 = fa.fa_decode_paged_run(*args, dev(torch.from_numpy(np.ascontiguousarray(plan))),
+                                      w.scale, wl, split, softcap=cap, alibi_slopes=sl_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
