@@ -377,7 +377,7 @@ def bench_others(fa, args):
         gbs = nb / ms / 1e6
         wl["paged_decode"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
                               "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb,
-                              "kernels": "decode_split_heads<128,4> (all split slots) + decode_merge"}
+                              "kernels": "decode_order + decode_split_heads<128,4> (device-made order) + decode_merge"}
     # plan / run split: the host plan lists only the (request, split) pairs that hold
     # keys, heaviest first; it is made once for the batch's lengths and its host time
     # is reported beside the run.  The decode roofline is this run's.

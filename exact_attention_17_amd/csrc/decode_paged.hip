@@ -699,6 +699,86 @@ static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
   }
 }
 
+// The unplanned call's work order, made on the device in one workgroup: every
+// (request, split) that holds a visible key, the full splits first (request
+// by request), then the partial ones (a request's first split under a window
+// and its last), then -1 for the remaining slots of the B x max_splits list,
+// which the split kernel skips.  Splits that end early go last, so the
+// launch's tail is short; the result does not depend on the order.
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads)
+void decode_order_kernel(DecodeParams p) {
+  __shared__ int scan_f[kOrderThreads], scan_p[kOrderThreads];
+  __shared__ int total_full;
+  const int tid = threadIdx.x;
+  const int S = p.split_tokens;
+  const int64_t cap_len = (int64_t)p.max_blocks * p.page_size;
+  // visible keys [lo, len) of request b: splits s0..s1, of which nf are full
+  auto range = [&](int b, int& s0, int& s1, int& lo, int& len) {
+    len = (int)min<int64_t>(max(p.seqlens[b], 0), cap_len);
+    lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
+    s0 = lo / S;
+    s1 = len > 0 ? (len - 1) / S : s0 - 1;
+  };
+  auto is_full = [&](int s, int lo, int len) { return max(s * S, lo) == s * S && min(len, s * S + S) == s * S + S; };
+  // exclusive scan of one value per thread over the workgroup (Hillis-Steele)
+  auto scan = [&](int* a, int v) {
+    a[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kOrderThreads; off <<= 1) {
+      const int add = tid >= off ? a[tid - off] : 0;
+      __syncthreads();
+      a[tid] += add;
+      __syncthreads();
+    }
+    const int incl = a[tid], total = a[kOrderThreads - 1];
+    __syncthreads();
+    return make_int2(incl - v, total);
+  };
+  auto counts = [&](int b, int& nf, int& np) {
+    nf = np = 0;
+    if (b >= p.B) return;
+    int s0, s1, lo, len;
+    range(b, s0, s1, lo, len);
+    for (int s = s0; s <= s1; ++s) (is_full(s, lo, len) ? nf : np) += 1;
+  };
+  // full items in total, so that the partial ones start after them
+  int mine = 0;
+  for (int b = tid; b < p.B; b += kOrderThreads) {
+    int nf, np;
+    counts(b, nf, np);
+    mine += nf;
+  }
+  const int2 tf = scan(scan_f, mine);
+  if (tid == 0) total_full = tf.y;
+  __syncthreads();
+  int base_f = 0, base_p = total_full;
+  for (int b0 = 0; b0 < p.B; b0 += kOrderThreads) {
+    const int b = b0 + tid;
+    int nf, np;
+    counts(b, nf, np);
+    const int2 ef = scan(scan_f, nf), ep = scan(scan_p, np);
+    if (b < p.B) {
+      int s0, s1, lo, len;
+      range(b, s0, s1, lo, len);
+      int wf = base_f + ef.x, wp = base_p + ep.x;
+      for (int s = s0; s <= s1; ++s) {
+        const int at = is_full(s, lo, len) ? wf++ : wp++;
+        p.order[2 * at] = b;
+        p.order[2 * at + 1] = s;
+      }
+    }
+    base_f += ef.y;
+    base_p += ep.y;
+  }
+  const int n_slots = p.B * p.max_splits;
+  for (int i = base_p + tid; i < n_slots; i += kOrderThreads) {
+    p.order[2 * i] = -1;
+    p.order[2 * i + 1] = -1;
+  }
+}
+
 // KV heads per workgroup of the head-set kernel, or 0 for the general one
 // (the head-set kernel's 16-token chunks start at multiples of 16 and must
 // not cross a page)
@@ -712,13 +792,24 @@ static int head_set(const DecodeParams& p) {
 }
 
 template <int D>
-static hipError_t launch_decode_d(const DecodeParams& p, int rows, hipStream_t stream) {
+static hipError_t launch_decode_d(const DecodeParams& p_in, int rows, hipStream_t stream) {
+  DecodeParams p = p_in;
+  // Without a host plan the split grid takes the device-made order when the
+  // 1-D grid over every slot fits; else one workgroup per (request, split) slot.
+  const int nh = head_set(p);
+  const int64_t per = nh > 0 ? (int64_t)p.Hkv / nh * p.sub_groups : (int64_t)p.Hkv * p.sub_groups;
+  if (!p.planned && (int64_t)p.B * p.max_splits * per * kDecodeThreads < ((int64_t)1 << 32)) {
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.planned = true;
+    p.plan = p.order;
+    p.num_items = p.B * p.max_splits;
+  }
   // an empty plan (every request has length 0): the merge alone writes O = 0
   if (!p.planned || p.num_items > 0) {
-    const int nh = head_set(p);
     if (nh > 0) {
-      const int per = p.Hkv / nh * p.sub_groups;
-      const dim3 grid = p.planned ? dim3(p.num_items * per) : dim3(per, p.max_splits, p.B);
+      const dim3 grid = p.planned ? dim3((unsigned)(p.num_items * per)) : dim3((unsigned)per, p.max_splits, p.B);
       if (nh == 4) hipLaunchKernelGGL((decode_split_heads_kernel<D, 4>), grid, dim3(kDecodeThreads), 0, stream, p);
       else hipLaunchKernelGGL((decode_split_heads_kernel<D, 2>), grid, dim3(kDecodeThreads), 0, stream, p);
     } else if (p.page_size % 16 == 0) {

@@ -297,13 +297,19 @@ static size_t part_o_bytes(int B, int Hq, int d, int max_splits) {
   return (n + 255) & ~(size_t)255;
 }
 
+// the unplanned call's device-made item list: (request, split) per slot
+static size_t order_bytes(int B, int max_splits) {
+  const size_t n = (size_t)B * max_splits * 2 * sizeof(int);
+  return (n + 255) & ~(size_t)255;
+}
+
 size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_blocks_per_seq,
                                       int page_size, int split_tokens) {
   if (!decode_sizes_ok(B, Hq, d, max_blocks_per_seq, page_size, split_tokens)) return 0;
   const int split = effective_split(split_tokens);
   const int max_splits = (int)cdiv((int64_t)max_blocks_per_seq * page_size, split);
   const size_t lse_bytes = ((size_t)B * Hq * max_splits * sizeof(float) + 255) & ~(size_t)255;
-  return part_o_bytes(B, Hq, d, max_splits) + lse_bytes;
+  return part_o_bytes(B, Hq, d, max_splits) + lse_bytes + order_bytes(B, max_splits);
 }
 
 }  // extern "C"
@@ -362,6 +368,8 @@ fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   p.max_splits = max_splits;
   p.part_o = static_cast<float*>(workspace);
   p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_o_bytes(B, Hq, d, p.max_splits));
+  p.order = reinterpret_cast<int*>(static_cast<char*>(workspace) + part_o_bytes(B, Hq, d, p.max_splits) +
+                                   ((((size_t)B * Hq * max_splits * sizeof(float)) + 255) & ~(size_t)255));
   p.scale_log2 = softmax_scale * kLog2e;
   p.win_left = norm_window(window_left);
   p.planned = planned;

@@ -117,6 +117,7 @@ struct DecodeParams {
   bool planned;            // false: grid over every (split, request) slot
   const int* plan;         // planned: (request, split) pairs, one per item
   int num_items;
+  int* order;              // workspace: the unplanned call's item list, made on the device
   // score modifiers, as in PrefillParams (cap_in = 0 and alibi = NULL: off)
   float cap_in, cap_out;
   const float* alibi;

@@ -152,8 +152,9 @@ fa_status fa_fwd_varlen_run(const void* q, const void* k, const void* v, void* o
 /*
  * Bytes of device workspace fa_decode_paged needs for these sizes (split
  * partials: one float32 row of d values plus one float32 LSE per request,
- * query head and split).  split_tokens = 0 selects the default of 512.
- * Returns 0 if the sizes are invalid.
+ * query head and split; and two int32 per (request, split) for the work
+ * order the call makes on the device).  split_tokens = 0 selects the
+ * default of 512.  Returns 0 if the sizes are invalid.
  */
 size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_blocks_per_seq,
                                       int page_size, int split_tokens);
@@ -164,7 +165,10 @@ size_t fa_decode_paged_workspace_size(int B, int Hq, int d, int max_blocks_per_s
  * "FIA / FlashAttention" explainer sec. 2).  Each request's one query row
  * attends to its cache_seqlens[b] cached tokens; the keys are cut into
  * chunks of split_tokens, each chunk yields a partial (LSE, O) and a second
- * kernel merges the partials by their log-sum-exp.
+ * kernel merges the partials by their log-sum-exp.  A one-workgroup kernel
+ * first lists, on the device, the splits that hold keys (full splits first),
+ * and the split kernel follows that list; the result is bit for bit that of
+ * fa_decode_paged_run with any plan.
  *   q, o     : (B, 1, Hq, d)
  *   k_cache, v_cache : [num_pages, page_size, Hkv, d]
  *   block_table : device int32 [B, max_blocks_per_seq]; token j of request b

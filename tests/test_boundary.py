@@ -129,10 +129,11 @@ def test_workspace_size(lib):
     # 64 requests, 32 heads, d 128, 512 blocks of 16 tokens, 512-token splits -> 16 splits
     n_o = 64 * 32 * 16 * 128 * 4
     n_l = 64 * 32 * 16 * 4
+    n_w = 64 * 16 * 2 * 4      # the device-made work order: one (request, split) pair per slot
     up = lambda x: (x + 255) // 256 * 256
-    assert ws(64, 32, 128, 512, 16, 512) == up(n_o) + up(n_l)
+    assert ws(64, 32, 128, 512, 16, 512) == up(n_o) + up(n_l) + up(n_w)
     assert ws(64, 32, 128, 512, 16, 0) == ws(64, 32, 128, 512, 16, 512)
-    assert ws(1, 1, 64, 1, 1, 16) == up(64 * 4) + up(4)
+    assert ws(1, 1, 64, 1, 1, 16) == up(64 * 4) + up(4) + up(8)
     for bad in [(0, 32, 128, 512, 16, 0), (1, 32, 96, 4, 16, 0), (1, 32, 128, 4, 16, 24),
                 (1, 32, 128, 0, 16, 0), (1, 32, 128, 4, 0, 0), (1, 32, 128, 4, 16, -16)]:
         assert ws(*bad) == 0
