@@ -547,3 +547,21 @@ def test_decode_score_modifiers(fa, case):
                                       w.scale, wl, split, softcap=cap, alibi_slopes=sl_dev)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(16, 4, 128), (8, 2, 64)])
+def test_decode_many_requests(fa, Hq, Hkv, d):
+    """More requests than the device-made work order takes per pass (1024):
+    lengths 0..90 with 16-token splits and a window mix empty requests, full
+    and partial splits; unplanned and planned results agree bit for bit."""
+    rng = np.random.default_rng(950 + Hq + d)
+    lens = [int(x) for x in rng.integers(0, 91, 2100)]
+    ps, split, wl = 16, 16, 40
+    npages = sum(-(-l // ps) for l in lens) + 3
+    w = workloads.random_paged(951 + d, lens, Hq, Hkv, d, ps, npages, split,
+                               max_blocks=6, window_left=wl)
+    o, lse = run_decode(fa, w)
+    O, LSE = decode_ref(w)
+    check(f"decode many requests h{Hq} kv{Hkv} d{d}", o, lse, O, LSE)
+    o2, lse2 = run_decode_planned(fa, w)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
