@@ -702,26 +702,30 @@ static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
 // The unplanned call's work order, made on the device in one workgroup: every
 // (request, split) that holds a visible key, the full splits first (request
 // by request), then the partial ones (a request's first split under a window
-// and its last), then -1 for the remaining slots of the B x max_splits list,
-// which the split kernel skips.  Splits that end early go last, so the
-// launch's tail is short; the result does not depend on the order.
+// and its last) by size, largest first (64 size buckets), then -1 for the
+// remaining slots of the B x max_splits list, which the split kernel skips.
+// Small splits go last, so the launch's tail is short; the result does not
+// depend on the order (within a bucket it is whatever the LDS counters give).
 constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = 64;
 
 __global__ __launch_bounds__(kOrderThreads)
 void decode_order_kernel(DecodeParams p) {
-  __shared__ int scan_f[kOrderThreads], scan_p[kOrderThreads];
-  __shared__ int total_full;
+  __shared__ int scan_f[kOrderThreads];
+  __shared__ int bucket_n[kOrderBuckets], bucket_at[kOrderBuckets];
+  __shared__ int total_items;
   const int tid = threadIdx.x;
   const int S = p.split_tokens;
   const int64_t cap_len = (int64_t)p.max_blocks * p.page_size;
-  // visible keys [lo, len) of request b: splits s0..s1, of which nf are full
+  // visible keys [lo, len) of request b lie in splits s0..s1
   auto range = [&](int b, int& s0, int& s1, int& lo, int& len) {
     len = (int)min<int64_t>(max(p.seqlens[b], 0), cap_len);
     lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
     s0 = lo / S;
     s1 = len > 0 ? (len - 1) / S : s0 - 1;
   };
-  auto is_full = [&](int s, int lo, int len) { return max(s * S, lo) == s * S && min(len, s * S + S) == s * S + S; };
+  auto keys_in = [&](int s, int lo, int len) { return min(len, s * S + S) - max(s * S, lo); };
+  auto bucket = [&](int keys) { return (int)(((int64_t)keys * kOrderBuckets - 1) / S); };   // 0..63
   // exclusive scan of one value per thread over the workgroup (Hillis-Steele)
   auto scan = [&](int* a, int v) {
     a[tid] = v;
@@ -736,44 +740,50 @@ void decode_order_kernel(DecodeParams p) {
     __syncthreads();
     return make_int2(incl - v, total);
   };
-  auto counts = [&](int b, int& nf, int& np) {
-    nf = np = 0;
-    if (b >= p.B) return;
-    int s0, s1, lo, len;
-    range(b, s0, s1, lo, len);
-    for (int s = s0; s <= s1; ++s) (is_full(s, lo, len) ? nf : np) += 1;
-  };
-  // full items in total, so that the partial ones start after them
+  if (tid < kOrderBuckets) bucket_n[tid] = 0;
+  __syncthreads();
+  // pass 1: full splits per thread, partial splits per size bucket
   int mine = 0;
   for (int b = tid; b < p.B; b += kOrderThreads) {
-    int nf, np;
-    counts(b, nf, np);
-    mine += nf;
+    int s0, s1, lo, len;
+    range(b, s0, s1, lo, len);
+    for (int s = s0; s <= s1; ++s) {
+      const int k = keys_in(s, lo, len);
+      if (k == S) ++mine;
+      else atomicAdd(&bucket_n[bucket(k)], 1);
+    }
   }
   const int2 tf = scan(scan_f, mine);
-  if (tid == 0) total_full = tf.y;
+  if (tid == 0) {
+    int at = tf.y;                      // partial splits follow the full ones, largest first
+    for (int k = kOrderBuckets - 1; k >= 0; --k) {
+      bucket_at[k] = at;
+      at += bucket_n[k];
+    }
+    total_items = at;
+  }
   __syncthreads();
-  int base_f = 0, base_p = total_full;
+  // pass 2: full splits in request order (scan offsets), partial ones by bucket
+  int base_f = 0;
   for (int b0 = 0; b0 < p.B; b0 += kOrderThreads) {
     const int b = b0 + tid;
-    int nf, np;
-    counts(b, nf, np);
-    const int2 ef = scan(scan_f, nf), ep = scan(scan_p, np);
+    int s0 = 0, s1 = -1, lo = 0, len = 0, nf = 0;
     if (b < p.B) {
-      int s0, s1, lo, len;
       range(b, s0, s1, lo, len);
-      int wf = base_f + ef.x, wp = base_p + ep.x;
-      for (int s = s0; s <= s1; ++s) {
-        const int at = is_full(s, lo, len) ? wf++ : wp++;
-        p.order[2 * at] = b;
-        p.order[2 * at + 1] = s;
-      }
+      for (int s = s0; s <= s1; ++s) nf += keys_in(s, lo, len) == S;
+    }
+    const int2 ef = scan(scan_f, nf);
+    int wf = base_f + ef.x;
+    for (int s = s0; s <= s1; ++s) {
+      const int k = keys_in(s, lo, len);
+      const int at = k == S ? wf++ : atomicAdd(&bucket_at[bucket(k)], 1);
+      p.order[2 * at] = b;
+      p.order[2 * at + 1] = s;
     }
     base_f += ef.y;
-    base_p += ep.y;
   }
   const int n_slots = p.B * p.max_splits;
-  for (int i = base_p + tid; i < n_slots; i += kOrderThreads) {
+  for (int i = total_items + tid; i < n_slots; i += kOrderThreads) {
     p.order[2 * i] = -1;
     p.order[2 * i + 1] = -1;
   }
