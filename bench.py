@@ -398,6 +398,22 @@ def bench_others(fa, args):
             "frac": round(gbs / PEAK_HBM_GBS, 4),
             "traffic": load_traffic("decode_paged_traffic", DECODE_SRC),
             "kernel": "decode_split_heads<128,4> (planned) + decode_merge", "avg_launch_ms": round(ms, 4)}
+    if not args.only_decode:
+        # the same cache and plan with 64 query heads (8 per KV head: two-KV-head sets);
+        # not a bench line of its own, reported beside it
+        q8 = workloads.device_normal(40, (64, 1, 64, 128))
+        o8, l8 = torch.empty_like(q8), torch.empty((64, 64), dtype=torch.float32, device="cuda")
+        ws8 = torch.empty(fa.fa_decode_paged_workspace_size(64, 64, 128, bt.shape[1], 16, 512),
+                          dtype=torch.uint8, device="cuda")
+        ms8 = time_calls(lambda: fa.fa_decode_paged_run(q8, kc, vc, bt, sl, plan_d, w4.scale, -1, 512,
+                                                        out=o8, lse=l8, workspace=ws8),
+                         args.steps, args.warmup, args.prewarm_ms)
+        nb8 = nb + 2 * 64 * 32 * 128 * 2 + 64 * 32 * 4     # q, o and lse of the 32 more heads
+        gbs8 = nb8 / ms8 / 1e6
+        wl["paged_decode_gqa8_planned"] = {"ms": round(ms8, 4), "GB/s": round(gbs8, 1),
+                                           "frac_hbm": round(gbs8 / PEAK_HBM_GBS, 4), "bytes": nb8,
+                                           "kernels": "decode_split_heads<128,2> (planned) + decode_merge"}
+        del q8, o8, l8, ws8
     del qd, kc, vc, w4, plan_d
     torch.cuda.empty_cache()
     return wl, roof
