@@ -530,7 +530,10 @@ void prefill_fwd_kernel(PrefillParams p) {
     for (int i = 0; i < 32 / ORPI; ++i) {
       const int r = 32 * wave + i * ORPI + lane / KCH, cc = lane % KCH;
       const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * RB + ((cc ^ (r & (KCH - 1))) * 16));
-      if (q0 + r < Lq) *reinterpret_cast<u32x4*>(og + (int64_t)(q0 + r) * p.q_tok_stride + 8 * cc) = val;
+      // non-temporal: O is written once, so it need not displace K/V tiles
+      // that other workgroups of the head still read from L2
+      if (q0 + r < Lq)
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(og + (int64_t)(q0 + r) * p.q_tok_stride + 8 * cc));
     }
   }
   if (row < Lq && lseg && hi == 0) lseg[row] = lt > 0.f ? (m_ref + log2_fast(lt)) * kLn2 : -INFINITY;
