@@ -506,7 +506,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int i = 0; i < 32 / ORPI; ++i) {
       const int r = 32 * blk + i * ORPI + lane / KCH, cc = lane % KCH;
       const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * RB + ((cc ^ (r & (KCH - 1))) * 16));
-      if (k0 + r < Lk) *reinterpret_cast<u32x4*>(out + (int64_t)(k0 + r) * p.k_tok_stride + 8 * cc) = val;
+      if (k0 + r < Lk)   // non-temporal: written once
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(out + (int64_t)(k0 + r) * p.k_tok_stride + 8 * cc));
     }
   }
 }
@@ -709,7 +710,8 @@ void bwd_dq_kernel(BwdParams p) {
     for (int i = 0; i < 32 / ORPI; ++i) {
       const int r = 32 * wave + i * ORPI + lane / KCH, cc = lane % KCH;
       const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * RB + ((cc ^ (r & (KCH - 1))) * 16));
-      if (q0 + r < Lq) *reinterpret_cast<u32x4*>(p.dq + q_off + (int64_t)(q0 + r) * p.q_tok_stride + 8 * cc) = val;
+      if (q0 + r < Lq)   // non-temporal: written once
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.dq + q_off + (int64_t)(q0 + r) * p.q_tok_stride + 8 * cc));
     }
   }
 }
