@@ -377,7 +377,8 @@ void decode_split_kernel(DecodeParams p) {
 // a load go to lanes l, l + 64/TPL, ..., added once at the end).
 constexpr int kQuadChunk = 16;   // tokens per wave iteration
 
-template <int D, int NH>
+// NT: one query subgroup, so every cache row is read by one workgroup only.
+template <int D, int NH, bool NT>
 __global__ __launch_bounds__(kDecodeThreads, 2)
 void decode_split_heads_kernel(DecodeParams p) {
   static_assert(NH == 4 || NH == 2, "four or two KV heads per workgroup");
@@ -483,13 +484,25 @@ void decode_split_heads_kernel(DecodeParams p) {
     // of 16); tokens outside [k_beg, k_end) are read but masked below
     const int pid = __builtin_amdgcn_readfirstlane(bt[kc / p.page_size]);
     const int64_t slot0 = (int64_t)pid * p.page_size + kc % p.page_size + tl;
+    // With one query subgroup each cache row is read once per step, and the
+    // loads are non-temporal so that they displace nothing in L2; further
+    // subgroups read the same rows again, from L2.
     u32x4 kr[LPC], vr[LPC];
+    if constexpr (NT) {
 #pragma unroll
-    for (int i = 0; i < LPC; ++i)
-      kr[i] = *reinterpret_cast<const u32x4*>(kcache + (slot0 + TPL * i) * tok_stride);
+      for (int i = 0; i < LPC; ++i)
+        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kcache + (slot0 + TPL * i) * tok_stride));
 #pragma unroll
-    for (int i = 0; i < LPC; ++i)
-      vr[i] = *reinterpret_cast<const u32x4*>(vcache + (slot0 + TPL * i) * tok_stride);
+      for (int i = 0; i < LPC; ++i)
+        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vcache + (slot0 + TPL * i) * tok_stride));
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPC; ++i)
+        kr[i] = *reinterpret_cast<const u32x4*>(kcache + (slot0 + TPL * i) * tok_stride);
+#pragma unroll
+      for (int i = 0; i < LPC; ++i)
+        vr[i] = *reinterpret_cast<const u32x4*>(vcache + (slot0 + TPL * i) * tok_stride);
+    }
     if (partial) {
 #pragma unroll
       for (int i = 0; i < LPC; ++i) {
@@ -820,8 +833,10 @@ static hipError_t launch_decode_d(const DecodeParams& p_in, int rows, hipStream_
   if (!p.planned || p.num_items > 0) {
     if (nh > 0) {
       const dim3 grid = p.planned ? dim3((unsigned)(p.num_items * per)) : dim3((unsigned)per, p.max_splits, p.B);
-      if (nh == 4) hipLaunchKernelGGL((decode_split_heads_kernel<D, 4>), grid, dim3(kDecodeThreads), 0, stream, p);
-      else hipLaunchKernelGGL((decode_split_heads_kernel<D, 2>), grid, dim3(kDecodeThreads), 0, stream, p);
+      const bool nt = p.sub_groups == 1;
+      if (nh == 4) hipLaunchKernelGGL((decode_split_heads_kernel<D, 4, true>), grid, dim3(kDecodeThreads), 0, stream, p);
+      else if (nt) hipLaunchKernelGGL((decode_split_heads_kernel<D, 2, true>), grid, dim3(kDecodeThreads), 0, stream, p);
+      else hipLaunchKernelGGL((decode_split_heads_kernel<D, 2, false>), grid, dim3(kDecodeThreads), 0, stream, p);
     } else if (p.page_size % 16 == 0) {
       launch_split<D, true>(p, rows, stream);
     } else {
