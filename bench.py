@@ -377,7 +377,7 @@ def bench_others(fa, args):
         gbs = nb / ms / 1e6
         wl["paged_decode"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
                               "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb,
-                              "kernels": "decode_order + decode_split_heads<128,4> (device-made order) + decode_merge"}
+                              "kernels": "decode_order + decode_split_heads<128,4,nt> (device-made order) + decode_merge"}
     # plan / run split: the host plan lists only the (request, split) pairs that hold
     # keys, heaviest first; it is made once for the batch's lengths and its host time
     # is reported beside the run.  The decode roofline is this run's.
@@ -393,11 +393,11 @@ def bench_others(fa, args):
                                   "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb,
                                   "plan_host_ms": round(plan_ms, 4),
                                   "plan_items": int(plan.shape[0]),
-                                  "kernels": "decode_split_heads<128,4> (planned) + decode_merge"}
+                                  "kernels": "decode_split_heads<128,4,nt> (planned) + decode_merge"}
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4),
             "traffic": load_traffic("decode_paged_traffic", DECODE_SRC),
-            "kernel": "decode_split_heads<128,4> (planned) + decode_merge", "avg_launch_ms": round(ms, 4)}
+            "kernel": "decode_split_heads<128,4,nt> (planned) + decode_merge", "avg_launch_ms": round(ms, 4)}
     if not args.only_decode:
         # the same cache and plan with 64 query heads (8 per KV head: two-KV-head sets);
         # not a bench line of its own, reported beside it
