@@ -751,3 +751,92 @@ def test_uint16_inputs_are_bf16_bit_patterns():
     v = bits.reshape(1, 1, 1, 5)
     O, _ = oracle.attention_ref(q, k, v, 1.0)
     assert np.array_equal(O[0, 0, 0], x.astype(np.float64))
+
+
+# ------------------------------------------------ sampled-row checker pins
+# attention_rows_ref checks every full-size prefill output on the GPU, so it is
+# pinned on its own: against the per-score brute force (which shares none of
+# its code) at b > 0, GQA heads, Lq != Lk, windows and both score modifiers,
+# and against attention_ref's rows on shapes with several row blocks.
+ROWS_CASES = [
+    # B, Lq, Lk, Hq, Hkv, causal, window, softcap, slopes shape
+    (3, 9, 9, 4, 2, True, (-1, -1), 0.0, None),
+    (2, 5, 11, 6, 2, True, (3, 0), 0.0, None),        # Lq < Lk, window, G = 3
+    (2, 10, 6, 4, 1, True, (-1, -1), 0.0, None),      # Lq > Lk: leading rows see no key
+    (3, 8, 8, 4, 4, False, (2, 1), 0.0, None),
+    (2, 7, 9, 4, 2, True, (-1, 2), 0.7, "h"),
+    (3, 6, 6, 6, 3, False, (-1, -1), 0.0, "bh"),
+    (2, 9, 12, 4, 2, True, (4, 0), 1.3, "bh"),
+]
+
+
+@pytest.mark.parametrize("case", ROWS_CASES)
+def test_rows_checker_matches_brute_force(case):
+    B, Lq, Lk, Hq, Hkv, causal, window, softcap, sh = case
+    rng = np.random.default_rng(400 + Lq * Lk + Hq)
+    d = 4
+    q, k, v = rng.standard_normal((B, Lq, Hq, d)), rng.standard_normal((B, Lk, Hkv, d)), \
+        rng.standard_normal((B, Lk, Hkv, d))
+    slopes = None if sh is None else rng.uniform(0.05, 0.7, Hq if sh == "h" else (B, Hq))
+    Ob, LSEb = brute_force_mod(q, k, v, 0.6, causal, *window, softcap,
+                               np.zeros(Hq) if slopes is None else slopes)
+    for b in range(B):
+        for h in range(Hq):
+            rows = rng.permutation(Lq)[:max(1, Lq // 2 + 1)]
+            O, LSE = oracle.attention_rows_ref(q, k, v, b, h, rows, 0.6, causal, window,
+                                               softcap=softcap, alibi_slopes=slopes)
+            want = LSEb[b, h, rows]
+            fin = np.isfinite(want)
+            assert np.array_equal(np.isfinite(LSE), fin), (b, h, rows)
+            assert np.abs(LSE[fin] - want[fin]).max(initial=0.0) < 1e-12
+            assert np.abs(O - Ob[b, rows, h]).max() < 1e-12
+
+
+@pytest.mark.parametrize("causal,window,softcap,sh", [(True, (-1, -1), 0.0, None),
+                                                       (True, (300, 0), 0.0, None),
+                                                       (False, (40, 90), 2.0, "bh"),
+                                                       (True, (-1, -1), 0.0, "h")])
+def test_rows_checker_matches_full_oracle_across_row_blocks(causal, window, softcap, sh):
+    """Rows on both sides of attention_ref's 1024-row block boundary, at b > 0
+    and on every query head of a GQA group."""
+    rng = np.random.default_rng(77)
+    B, Lq, Lk, Hq, Hkv, d = 2, 1100, 1300, 4, 2, 8
+    q, k, v = rng.standard_normal((B, Lq, Hq, d)), rng.standard_normal((B, Lk, Hkv, d)), \
+        rng.standard_normal((B, Lk, Hkv, d))
+    slopes = None if sh is None else rng.uniform(0.0, 0.05, Hq if sh == "h" else (B, Hq))
+    O, LSE = oracle.attention_ref(q, k, v, 0.3, causal, window, softcap=softcap,
+                                  alibi_slopes=slopes)
+    rows = np.array([0, 1, 511, 1022, 1023, 1024, 1025, Lq - 1])
+    for b in range(B):
+        for h in range(Hq):
+            Or, LSEr = oracle.attention_rows_ref(q, k, v, b, h, rows, 0.3, causal, window,
+                                                 softcap=softcap, alibi_slopes=slopes)
+            assert np.abs(Or - O[b, rows, h]).max() < 1e-12
+            assert np.abs(LSEr - LSE[b, h, rows]).max() < 1e-12
+
+
+def test_rows_checker_planted_mistakes_are_caught(monkeypatch):
+    """Mistakes a sampled-row checker could make -- reading batch 0, the wrong KV
+    head, rows counted from the top instead of bottom-right -- fail the pins."""
+    rng = np.random.default_rng(5)
+    q, k, v = rng.standard_normal((2, 5, 4, 3)), rng.standard_normal((2, 8, 2, 3)), \
+        rng.standard_normal((2, 8, 2, 3))
+    Ob, LSEb = brute_force_mod(q, k, v, 0.8, True, -1, -1, 0.0, np.zeros(4))
+
+    def agrees(fn):
+        rows = np.arange(5)
+        for b in range(2):
+            for h in range(4):
+                O, _ = fn(q, k, v, b, h, rows, 0.8, True)
+                if np.abs(O - Ob[b, rows, h]).max() > 1e-12:
+                    return False
+        return True
+
+    assert agrees(oracle.attention_rows_ref)
+    orig = oracle_attention.attention_rows_ref
+    assert not agrees(lambda q_, k_, v_, b, h, rows, *a: orig(q_, k_, v_, 0, h, rows, *a))
+    assert not agrees(lambda q_, k_, v_, b, h, rows, *a: orig(q_, k_, v_, b, h % 2 * 2, rows, *a))
+    orig_vis = oracle_attention.key_visibility
+    monkeypatch.setattr(oracle_attention, "key_visibility",
+                        lambda Lq, Lk, c, wl=-1, wr=-1, rows=None: orig_vis(Lk, Lk, c, wl, wr, rows=rows))
+    assert not agrees(oracle_attention.attention_rows_ref)
