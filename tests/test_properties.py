@@ -126,3 +126,32 @@ def test_repeated_runs_are_bitwise_identical(fa):
         for _ in range(30):
             o, lse = fa.fa_fwd(q, k, v, w.scale, causal, window)
             assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), case
+
+
+def test_side_stream_calls_match_current_stream_calls(fa):
+    """Calls on a side stream (buffers the binding allocates live on that stream)
+    return bitwise what calls on the current stream return; the side stream's
+    results are read after it is synchronised, while the current stream keeps
+    allocating and writing other tensors."""
+    w = workloads.random_dense(15, 2, 300, 300, 8, 2, 128, True)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    p = workloads.random_paged(16, [700, 90, 1300], 8, 2, 128, 16, 160, 512)
+    pq, kc, vc = dev(p.q), dev(p.k_cache), dev(p.v_cache)
+    bt, sl = dev(torch.as_tensor(p.block_table)), dev(torch.as_tensor(p.seqlens))
+    do = dev(workloads.upstream_grad(17, tuple(w.q.shape)))
+    ref_f = fa.fa_fwd(q, k, v, w.scale, True)
+    ref_d = fa.fa_decode_paged(pq, kc, vc, bt, sl, p.scale, -1, 512)
+    ref_b = fa.fa_bwd(q, k, v, ref_f[0], ref_f[1], do, w.scale, True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        f = fa.fa_fwd(q, k, v, w.scale, True, stream=side)
+        d = fa.fa_decode_paged(pq, kc, vc, bt, sl, p.scale, -1, 512, stream=side)
+        g = fa.fa_bwd(q, k, v, ref_f[0], ref_f[1], do, w.scale, True, stream=side)
+        junk = [torch.full((1 << 20,), 3.0, device="cuda") for _ in range(8)]   # current stream
+        side.synchronize()
+        for a, b in zip(list(f) + list(d) + list(g), list(ref_f) + list(ref_d) + list(ref_b)):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+        del junk
