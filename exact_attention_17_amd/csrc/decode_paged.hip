@@ -46,6 +46,12 @@
 
 namespace fa {
 
+// Request b's key count, clamped to [0, max_blocks * page_size] (the block
+// table's capacity); every decode kernel reads lengths through this.
+FA_DEV inline int clamp_len(const DecodeParams& p, int b) {
+  return (int)min((int64_t)max(p.seqlens[b], 0), (int64_t)p.max_blocks * p.page_size);
+}
+
 namespace {
 constexpr float kRescaleTau = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -109,7 +115,9 @@ void decode_split_kernel(DecodeParams p) {
   const int h0 = kvh * p.group + sub * GR;
   const int nrow = min(GR, p.group - sub * GR);
 
-  const int len = p.seqlens[b];
+  // lengths past the block table's capacity are out of contract; clamped as in
+  // the order kernel and the host plan, so no read leaves the table or the partials
+  const int len = clamp_len(p, b);
   const int lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
   const int split_base = s * p.split_tokens;
   const int k_beg = max(split_base, lo);
@@ -421,7 +429,9 @@ void decode_split_heads_kernel(DecodeParams p) {
   const int hs = hsub / p.sub_groups, q0 = (hsub - hs * p.sub_groups) * GM;
   const int G = p.group;
 
-  const int len = p.seqlens[b];
+  // lengths past the block table's capacity are out of contract; clamped as in
+  // the order kernel and the host plan, so no read leaves the table or the partials
+  const int len = clamp_len(p, b);
   const int lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
   const int split_base = s * p.split_tokens;
   const int k_beg = max(split_base, lo);
@@ -655,7 +665,9 @@ __global__ __launch_bounds__(64)
 void decode_merge_kernel(DecodeParams p) {
   constexpr int PER = D / 64;
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int len = p.seqlens[b];
+  // lengths past the block table's capacity are out of contract; clamped as in
+  // the order kernel and the host plan, so no read leaves the table or the partials
+  const int len = clamp_len(p, b);
   const int lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
   const int s_beg = lo / p.split_tokens;
   const int s_end = (len + p.split_tokens - 1) / p.split_tokens;
@@ -729,10 +741,9 @@ void decode_order_kernel(DecodeParams p) {
   __shared__ int total_items;
   const int tid = threadIdx.x;
   const int S = p.split_tokens;
-  const int64_t cap_len = (int64_t)p.max_blocks * p.page_size;
   // visible keys [lo, len) of request b lie in splits s0..s1
   auto range = [&](int b, int& s0, int& s1, int& lo, int& len) {
-    len = (int)min<int64_t>(max(p.seqlens[b], 0), cap_len);
+    len = clamp_len(p, b);
     lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
     s0 = lo / S;
     s1 = len > 0 ? (len - 1) / S : s0 - 1;

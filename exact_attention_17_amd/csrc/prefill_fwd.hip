@@ -374,26 +374,22 @@ void prefill_fwd_kernel(PrefillParams p) {
   // then each MFMA followed by some softmax VALU ops and the next LDS reads,
   // so reads stay a few MFMAs ahead and the VALU work hides under the MFMAs.
   auto interleave_hint = [](auto with_pv) {
-#ifndef IL_UP
-#define IL_UP 3
-#define IL_V1 4
-#define IL_R1 1
-#define IL_V2 3
-#define IL_R2 2
-#endif
-    __builtin_amdgcn_sched_group_barrier(0x100, IL_UP, 0);
+    // fixed schedule: K fragment reads issued up front, then per S^T MFMA
+    // 4 VALU ops and 1 read, per P V MFMA 3 VALU ops and 2 reads
+    constexpr int kReadsUp = 3, kValuQk = 4, kReadsQk = 1, kValuPv = 3, kReadsPv = 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, kReadsUp, 0);
 #pragma unroll
     for (int i = 0; i < 2 * KSTEPS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, IL_V1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, IL_R1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuQk, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kReadsQk, 0);
     }
     if constexpr (decltype(with_pv)::value) {
 #pragma unroll
       for (int i = 0; i < 4 * DBLK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, IL_V2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, IL_R2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPv, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kReadsPv, 0);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
