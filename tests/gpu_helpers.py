@@ -42,3 +42,35 @@ def check(name, o, lse, o_ref, lse_ref):
     assert ratio <= 1.0, f"{name}: O error {ratio:.3f} x tolerance"
     assert dl <= LSE_TOL, f"{name}: LSE error {dl:.3e}"
     return ratio, dl
+
+
+def oracle_rows_parallel(q, k, v, tasks, scale, causal, window, workers=None):
+    """oracle.attention_rows_ref over many (b, h, rows) tasks, run in a thread pool
+    (numpy's kernels release the GIL; BLAS is held to one thread per task so the
+    pool does not oversubscribe the host).  q, k, v: bf16 bit patterns (uint16)
+    of the dense (B, L, H, d) layout.  Returns a list of (O, LSE) per task."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                      # pragma: no cover - installed here
+        threadpool_limits = None
+    n = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+
+    def one(t):
+        b, h, rows = t
+        return oracle.attention_rows_ref(q, k, v, b, h, rows, scale, causal, window)
+
+    if threadpool_limits is None:
+        with ThreadPoolExecutor(n) as ex:
+            return list(ex.map(one, tasks))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(n) as ex:
+        return list(ex.map(one, tasks))
+
+
+def nan_like(t):
+    """A device tensor of t's shape and dtype filled with NaN: outputs start
+    poisoned, so an element the kernels never write fails the finiteness check."""
+    return torch.full_like(t, float("nan"))

@@ -5,9 +5,9 @@ several 128-row / 64-key tiles with ragged tails and cover each mask mode,
 MHA/GQA/MQA, both head dims, Lq != Lk, fully masked rows, zero-length varlen
 sequences, plans in heaviest-first, shuffled and partial order, and paged
 layouts with several page sizes and split sizes.  The five
-named workloads run at full size in the launch configuration bench.py times;
-prefill outputs are checked on sampled rows the oracle computes one by one,
-the decode workload on every output.
+named workloads run at full size in the launch configuration bench.py times,
+with outputs NaN-poisoned before the call, and every output element of each is
+compared with the oracle.
 """
 
 import math
@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import bits, check, dev, f64
+from gpu_helpers import bits, check, dev, f64, nan_like, oracle_rows_parallel
 
 pytestmark = pytest.mark.gpu
 
@@ -333,42 +333,56 @@ def test_varlen_run_any_order_and_partial_plans(fa):
 
 
 # ---------------------------------------------------------- full workloads
-def sampled_rows(L, rng, extra=12):
-    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, L // 2, L - 129, L - 128, L - 2, L - 1]
-    rnd = rng.integers(0, L, extra).tolist()
-    return np.unique(np.clip(fixed + rnd, 0, L - 1))
+# The named workloads at full size, in the launch configuration bench.py times.
+# Outputs start NaN-poisoned, so an element no workgroup writes fails, and
+# every output element is compared with the oracle (row blocks of at most 1024
+# query rows, run in a thread pool on the host).
+def rows_in_blocks(rows, block=1024):
+    rows = np.asarray(rows)
+    return [rows[i:i + block] for i in range(0, len(rows), block)]
 
 
-def check_dense_sampled(name, w, o, lse, pairs, rng):
+def run_dense_poisoned(fa, w):
+    q = dev(w.q)
+    B, Lq, Hq, _ = w.q.shape
+    out = nan_like(q)
+    lse = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device="cuda")
+    o, l = fa.fa_fwd(q, dev(w.k), dev(w.v), w.scale, w.causal, w.window, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr() and l.data_ptr() == lse.data_ptr()
+    return f64(o.cpu()), f64(l.cpu())
+
+
+def check_dense_tasks(name, w, o_np, lse_np, tasks):
+    """Every output finite, then each (b, h, rows) task against the oracle."""
+    assert np.isfinite(o_np).all(), f"{name}: non-finite (unwritten?) output"
+    assert np.isfinite(lse_np).all(), f"{name}: non-finite (unwritten?) LSE"
     qb, kb, vb = bits(w.q), bits(w.k), bits(w.v)
-    o_np, lse_np = f64(o), f64(lse)
-    assert np.isfinite(o_np).all() and np.isfinite(lse_np).all()
-    vmax = np.abs(f64(w.v)).max()
-    assert np.abs(o_np).max() <= vmax * (1 + 1e-2) + 4e-3        # convex combination of V rows
-    L = w.q.shape[1]
+    refs = oracle_rows_parallel(qb, kb, vb, tasks, w.scale, w.causal, w.window)
     worst = (0.0, 0.0)
-    for b, h in pairs:
-        rows = sampled_rows(L, rng)
-        O, LSE = oracle.attention_rows_ref(qb, kb, vb, b, h, rows, w.scale, w.causal, w.window)
-        r = check(f"{name} b{b} h{h}", o_np[b, rows, h], lse_np[b, h, rows], O, LSE)
+    for (b, h, rows), (O, LSE) in zip(tasks, refs):
+        r = check(f"{name} b{b} h{h} rows {rows[0]}..{rows[-1]} ({len(rows)})",
+                  o_np[b, rows, h], lse_np[b, h, rows], O, LSE)
         worst = (max(worst[0], r[0]), max(worst[1], r[1]))
+    print(f"[parity] {name}: {len(tasks)} row blocks, worst err/tol {worst[0]:.3f}, "
+          f"worst |dLSE| {worst[1]:.2e}", flush=True)
     return worst
 
 
 def test_full_causal_mha(fa):
     w = workloads.causal_mha()
-    o, lse = run_dense(fa, w)
-    rng = np.random.default_rng(2)
-    pairs = [(0, 0), (1, 7), (2, 19), (3, 31), (3, 0), (0, 16)]
-    check_dense_sampled(w.name, w, o, lse, pairs, rng)
+    o, lse = run_dense_poisoned(fa, w)
+    B, L, H, _ = w.q.shape
+    tasks = [(b, h, rows) for b in range(B) for h in range(H) for rows in rows_in_blocks(np.arange(L))]
+    check_dense_tasks(w.name, w, o, lse, tasks)
 
 
 def test_full_causal_gqa_long(fa):
     w = workloads.causal_gqa_long()
-    o, lse = run_dense(fa, w)
-    rng = np.random.default_rng(3)
-    pairs = [(0, 0), (0, 3), (0, 4), (0, 17), (0, 30), (0, 31)]
-    check_dense_sampled(w.name, w, o, lse, pairs, rng)
+    o, lse = run_dense_poisoned(fa, w)
+    _, L, H, _ = w.q.shape
+    tasks = [(0, h, rows) for h in range(H) for rows in rows_in_blocks(np.arange(L))]
+    check_dense_tasks(w.name, w, o, lse, tasks)
 
 
 @pytest.mark.parametrize("planned", [False, True], ids=["all_split_slots", "planned"])
@@ -383,25 +397,32 @@ def test_full_paged_decode(fa, planned):
 def test_full_varlen_window(fa, planned):
     w = workloads.varlen_window()
     cu = dev(torch.from_numpy(w.cu_seqlens))
+    q = dev(w.q)
+    T, H, _ = w.q.shape
+    out = nan_like(q)
+    lse_buf = torch.full((H, T), float("nan"), dtype=torch.float32, device="cuda")
     if planned:
-        o, lse = run_planned(fa, w)
+        o, lse = run_planned(fa, w, out=out, lse=lse_buf)
     else:
-        o, lse = fa.fa_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), cu, cu, w.max_seqlen,
-                                  w.max_seqlen, w.scale, w.causal, w.window)
+        o, lse = fa.fa_fwd_varlen(q, dev(w.k), dev(w.v), cu, cu, w.max_seqlen,
+                                  w.max_seqlen, w.scale, w.causal, w.window, out=out, lse=lse_buf)
         torch.cuda.synchronize()
     o, lse = f64(o.cpu()), f64(lse.cpu())
-    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), "unwritten varlen output"
+    # each packed sequence is the dense definition on its own slice (a batch of one)
     qb, kb, vb = bits(w.q), bits(w.k), bits(w.v)
-    rng = np.random.default_rng(5)
-    H = w.q.shape[1]
+    worst = (0.0, 0.0)
     for b, L in enumerate(w.lens):
-        s = int(w.cu_seqlens[b])
-        rows = sampled_rows(int(L), rng, extra=4)
-        rows = np.unique(np.concatenate([rows, np.clip([4095, 4096, 4097, 4098], 0, L - 1)]))
-        for h in (b % H, (b * 7 + 3) % H):
-            O, LSE = oracle.attention_rows_ref(qb[None, s:s + L], kb[None, s:s + L], vb[None, s:s + L],
-                                               0, h, rows, w.scale, w.causal, w.window)
-            check(f"{w.name} seq{b} h{h}", o[s + rows, h], lse[h, s + rows], O, LSE)
+        s, L = int(w.cu_seqlens[b]), int(L)
+        sub = [(0, h, rows) for h in range(H) for rows in rows_in_blocks(np.arange(L))]
+        refs = oracle_rows_parallel(qb[None, s:s + L], kb[None, s:s + L], vb[None, s:s + L], sub,
+                                    w.scale, w.causal, w.window)
+        for (_, h, rows), (O, LSE) in zip(sub, refs):
+            r = check(f"{w.name} seq{b} h{h} rows {rows[0]}..{rows[-1]}", o[s + rows, h],
+                      lse[h, s + rows], O, LSE)
+            worst = (max(worst[0], r[0]), max(worst[1], r[1]))
+    print(f"[parity] {w.name}: every element, worst err/tol {worst[0]:.3f}, "
+          f"worst |dLSE| {worst[1]:.2e}", flush=True)
 
 
 # ------------------------------------------- chunked prefill over a paged cache
