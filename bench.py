@@ -1,28 +1,31 @@
 """Benchmark of the fused attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--only {main,causal_mha,varlen_window,decode,bwd}]
 
-A step is one fa_fwd call on the causal MHA prefill workload (B=4, H=32,
-L=2048, d=128, bf16, seeded synthetic inputs resident in HBM).  The timed
-region is exactly K steps bracketed by torch.cuda.synchronize(); `value` is
-algorithmic TFLOP/s (4*d FLOPs per visible (query, key) pair per head).
+A step is one fa_fwd call on the long-context causal GQA prefill workload
+(B=1, Hq=32, Hkv=8, L=16384, d=128, bf16, seeded synthetic inputs resident in
+HBM), the largest workload that the metric covers.  The timed region is
+exactly K steps bracketed by torch.cuda.synchronize(); `value` is algorithmic
+TFLOP/s (4*d FLOPs per visible (query, key) pair per query head) over that
+wall time.  Each step is also bracketed by HIP events recorded on the launch
+stream (torch's current stream, which the binding launches on), which give the
+per-launch mean, median and minimum.
 
 Before the W warmup steps each workload runs untimed for --prewarm-ms of wall
 time: the GPU raises its engine clock only after some milliseconds of
-sustained load, and without this the first tens of milliseconds (the whole
-timed region at small K) run at a lower clock.
-The other workloads (long-context GQA prefill, paged decode, varlen window
-prefill, the small dense case, and a chunk of 512 new tokens appended to and
-attending over a paged cache) are timed in the same run and reported under
-"workloads".  One JSON line is printed.
+sustained load.
 
-"roofline" covers the dominant kernel (the prefill kernel on the main
-workload): achieved = algorithmic FLOPs per launch / the launch's average
-duration from HIP events on the launch stream, against the bf16 dense MFMA
-peak.  "traffic" comes from the committed rocprofv3 counter summary for that
-kernel and is null if the kernel source changed since it was taken.
-"cpu_baseline" times the CPU fp64 oracle on a bounded sample of the same
-workload on this host.
+"roofline" covers the dominant kernel of the step (the prefill kernel on the
+main workload): achieved = algorithmic FLOPs per launch / mean launch
+duration from those events, against the bf16 dense MFMA peak.  "traffic" is
+HBM bytes per launch from the committed rocprofv3 counter summary for that
+kernel and workload, null if the kernel source changed since it was taken.
+The causal MHA prefill (B=4, H=32, L=2048) and the paged decode call
+(fa_decode_paged, no host plan) carry roofline blocks of their own; the other
+workloads are reported under "workloads".  "cpu_baseline" times the CPU fp64
+oracle on a bounded sample of the main workload on this host, and per
+workload under "cpu_baseline.per_workload".  One JSON line is printed.
 """
 
 import argparse
@@ -30,6 +33,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -48,6 +52,7 @@ PREFILL_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "prefill_fwd.
 DECODE_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "decode_paged.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 << 20             # plain device copy used to calibrate the byte counters
+PREFILL_KERNEL = "prefill_fwd_kernel<128, 0, false>"
 
 
 def visible_pairs(Lq, Lk, causal, wl, wr):
@@ -97,20 +102,50 @@ def prewarm(fn, ms):
         torch.cuda.synchronize()
 
 
-def time_calls(fn, steps, warmup, prewarm_ms=0.0):
-    """Average ms per call from HIP events recorded on the launch stream
-    (torch's current stream, which the binding launches on)."""
+def timed_steps(fn, steps, warmup, prewarm_ms):
+    """Pre-warm, W warmup calls, then exactly `steps` calls between two
+    synchronisations, each call bracketed by HIP events on the launch stream.
+    Returns wall ms per call and the per-call event durations (ms)."""
     prewarm(fn, prewarm_ms)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record()
         fn()
-    e.record()
+        e.record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, [s.elapsed_time(e) for s, e in ev]
+
+
+def stats(durations):
+    return {"mean": statistics.fmean(durations), "median": statistics.median(durations),
+            "min": min(durations)}
+
+
+def rate_entry(work, durations, unit, peak, scale):
+    """Per-workload entry: ms (mean / median / min) and the rate at the mean."""
+    st = stats(durations)
+    rate = work / st["mean"] / scale
+    out = {"ms": round(st["mean"], 4), "median_ms": round(st["median"], 4),
+           "min_ms": round(st["min"], 4), "calls": len(durations), unit: round(rate, 2)}
+    out["frac_mfma" if unit == "TFLOP/s" else "frac_hbm"] = round(rate / peak, 4)
+    return out
+
+
+def roofline_block(bound, work, durations, unit, peak, scale, traffic, kernel):
+    st = stats(durations)
+    ach = work / st["mean"] / scale
+    return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": traffic, "kernel": kernel,
+            "avg_launch_ms": round(st["mean"], 4), "median_launch_ms": round(st["median"], 4),
+            "min_launch_ms": round(st["min"], 4),
+            "frac_at_median": round(work / st["median"] / scale / peak, 4),
+            "launches": len(durations)}
 
 
 def load_traffic(summary_name, src):
@@ -140,47 +175,318 @@ def copy_calibration(reps=5):
     del src, dst
 
 
-def cpu_baseline(w, flops_total):
-    """Time the CPU fp64 oracle on a bounded sample of the workload."""
-    import oracle
+# ------------------------------------------------------------------ CPU oracle
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    B, L, Hq, d = w.q.shape
-    pairs = [(b, h) for b in range(B) for h in range(Hq)]     # the whole step (a few seconds)
-    qb = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
-    kb = w.k.contiguous().view(torch.int16).numpy().view(np.uint16)
-    vb = w.v.contiguous().view(torch.int16).numpy().view(np.uint16)
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
+
+
+def u16(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def time_oracle_dense(w, heads, flops_total):
+    """The oracle on every row of the given (batch, head) pairs of a dense workload."""
+    import oracle
+    B, L, Hq, _ = w.q.shape
+    qb, kb, vb = u16(w.q), u16(w.k), u16(w.v)
     t0 = time.perf_counter()
-    for b, h in pairs:
-        oracle.attention_rows_ref(qb, kb, vb, b, h, np.arange(L), w.scale, w.causal, w.window)
+    for b, h in heads:
+        for r0 in range(0, L, 1024):
+            oracle.attention_rows_ref(qb, kb, vb, b, h, np.arange(r0, min(L, r0 + 1024)),
+                                      w.scale, w.causal, w.window)
     dt = time.perf_counter() - t0
-    sample_flops = flops_total * len(pairs) / (B * Hq)
-    return {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"all {len(pairs)} (batch, head) pairs of {w.name} (one whole step), all {L} "
-                      "rows each, full S and P in float64 (numpy)"}
+    return dt, flops_total * len(heads) / (B * Hq)
+
+
+def cpu_baseline(main_w, main_flops, per_workload):
+    """The oracle (plain numpy fp64, as it is) on a bounded sample of the main
+    workload, plus bounded samples of the others: seconds and the algorithmic rate
+    of each sample."""
+    heads = [(0, 0), (0, 31)]                    # 2 of 32 query heads, every row
+    dt, fl = time_oracle_dense(main_w, heads, main_flops)
+    out = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(),
+           "kind": "oracle", "seconds": round(dt, 2), "cpu_model": cpu_model(),
+           "sample": f"query heads 0 and 31 (2 of 32) of {main_w.name}, all 16384 rows each "
+                     "(1/16 of one step), full S and P rows in float64 (numpy)"}
+    if per_workload:
+        out["per_workload"] = per_workload_oracle()
+    return out
+
+
+def per_workload_oracle():
+    import oracle
+    res = {}
+    w1 = workloads.small_dense(Hkv=1)
+    t0 = time.perf_counter()
+    oracle.attention_ref(u16(w1.q), u16(w1.k), u16(w1.v), w1.scale, w1.causal, w1.window)
+    dt = time.perf_counter() - t0
+    res[w1.name] = {"seconds": round(dt, 4), "sample": "whole step",
+                    "GFLOP/s": round(dense_flops(w1) / dt / 1e9, 3)}
+    w2 = workloads.causal_mha()
+    dt, fl = time_oracle_dense(w2, [(0, h) for h in range(32)], dense_flops(w2))
+    res[w2.name] = {"seconds": round(dt, 2), "sample": "batch 0, all 32 heads (1/4 of a step)",
+                    "GFLOP/s": round(fl / dt / 1e9, 2)}
+    del w2
+    w4 = workloads.paged_decode()
+    n = 16
+    t0 = time.perf_counter()
+    oracle.decode_paged_ref(u16(w4.q[:n]), u16(w4.k_cache), u16(w4.v_cache), w4.block_table[:n],
+                            w4.seqlens[:n], w4.page_size, w4.scale)
+    dt = time.perf_counter() - t0
+    sub = workloads.Paged(w4.name, w4.q[:n], w4.k_cache, w4.v_cache, w4.block_table[:n],
+                          w4.seqlens[:n], w4.page_size, w4.split_tokens, w4.scale)
+    res[w4.name] = {"seconds": round(dt, 2), "sample": f"requests 0..{n - 1} (of 64)",
+                    "GB/s": round(decode_bytes(sub) / dt / 1e9, 3)}
+    del w4, sub
+    w5 = workloads.varlen_window()
+    heads = [0, 15]
+    q5, k5, v5 = (u16(t[:, heads]) for t in (w5.q, w5.k, w5.v))
+    cu = w5.cu_seqlens
+    t0 = time.perf_counter()
+    oracle.attention_varlen_ref(q5, k5, v5, cu, cu, w5.scale, w5.causal, w5.window)
+    dt = time.perf_counter() - t0
+    res[w5.name] = {"seconds": round(dt, 2), "sample": "heads 0 and 15 (2 of 16), every sequence",
+                    "GFLOP/s": round(varlen_flops(w5) * len(heads) / 16 / dt / 1e9, 2)}
+    return res
+
+
+# ------------------------------------------------------------------ GPU parts
+def bench_main(fa, w3, flops3, args):
+    """The contract step: K timed fa_fwd calls on the long-context GQA workload."""
+    q, k, v = w3.q.cuda(), w3.k.cuda(), w3.v.cuda()
+    B, L, Hq, d = w3.q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    step = lambda: fa.fa_fwd(q, k, v, w3.scale, True, (-1, -1), out=o, lse=lse)
+    wall, dur = timed_steps(step, args.steps, args.warmup, args.prewarm_ms)
+    st = stats(dur)
+    return {
+        "value": round(flops3 / (wall * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "ms_per_step": round(wall, 4), "median_ms": round(st["median"], 4),
+        "min_ms": round(st["min"], 4),
+        "config": {"workload": w3.name, "B": B, "Hq": Hq, "Hkv": w3.k.shape[2], "L": L, "d": d,
+                   "causal": True, "flops_per_step": flops3},
+        "roofline": roofline_block("mfma", flops3, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9,
+                                   load_traffic("prefill_fwd_causal_gqa_long_traffic", PREFILL_SRC),
+                                   PREFILL_KERNEL),
+    }
+
+
+def bench_causal_mha(fa, args):
+    w2 = workloads.causal_mha()
+    q, k, v = w2.q.cuda(), w2.k.cuda(), w2.v.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((4, 32, 2048), dtype=torch.float32, device="cuda")
+    f2 = dense_flops(w2)
+    _, dur = timed_steps(lambda: fa.fa_fwd(q, k, v, w2.scale, True, (-1, -1), out=o, lse=lse),
+                         args.steps, args.warmup, args.prewarm_ms)
+    roof = roofline_block("mfma", f2, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9,
+                          load_traffic("prefill_fwd_causal_mha_traffic", PREFILL_SRC),
+                          PREFILL_KERNEL)
+    roof["workload"] = w2.name
+    entry = rate_entry(f2, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9)
+    entry["flops"] = f2
+    return entry, roof
+
+
+def bench_varlen(fa, args):
+    wl = {}
+    w5 = workloads.varlen_window()
+    a = [t.cuda() for t in (w5.q, w5.k, w5.v)]
+    cu = torch.from_numpy(w5.cu_seqlens).cuda()
+    f5 = varlen_flops(w5)
+    o = torch.empty_like(a[0])
+    lse = torch.empty((16, a[0].shape[0]), dtype=torch.float32, device="cuda")
+    _, dur = timed_steps(lambda: fa.fa_fwd_varlen(*a, cu, cu, w5.max_seqlen, w5.max_seqlen,
+                                                  w5.scale, True, w5.window, out=o, lse=lse),
+                         args.steps, args.warmup, args.prewarm_ms)
+    wl["varlen_window"] = rate_entry(f5, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9)
+    wl["varlen_window"]["flops"] = f5
+    # plan / run split: the host plan (heaviest tiles first) is made once for the
+    # batch's lengths and reused; its host time is reported beside the run
+    t0 = time.perf_counter()
+    plan = fa.fa_varlen_plan(w5.cu_seqlens, w5.cu_seqlens, True, w5.window)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    plan_d = torch.from_numpy(plan).cuda()
+    _, dur = timed_steps(lambda: fa.fa_fwd_varlen_run(*a, cu, cu, plan_d, w5.max_seqlen,
+                                                      w5.max_seqlen, w5.scale, True, w5.window,
+                                                      out=o, lse=lse),
+                         args.steps, args.warmup, args.prewarm_ms)
+    e = rate_entry(f5, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9)
+    e.update({"flops": f5, "plan_host_ms": round(plan_ms, 4), "plan_items": int(plan.shape[0])})
+    wl["varlen_window_planned"] = e
+    return wl
+
+
+def bench_bwd(fa, args, all_workloads):
+    """Backward: prep + dK/dV + dQ kernels; algorithmic work = the five products of
+    the chain rule (S, dP, dV, dK, dQ), 2.5x the forward."""
+    wl = {}
+    w2 = workloads.causal_mha()
+    a = [t.cuda() for t in (w2.q, w2.k, w2.v)]
+    do2 = workloads.upstream_grad(1002, tuple(w2.q.shape)).cuda()
+    o2, l2 = fa.fa_fwd(*a, w2.scale, True)
+    gq, gk, gv = torch.empty_like(a[0]), torch.empty_like(a[1]), torch.empty_like(a[2])
+    ws2 = torch.empty(fa.fa_bwd_workspace_size(4, 32, 2048), dtype=torch.uint8, device="cuda")
+    fb = 2.5 * dense_flops(w2)
+    _, dur = timed_steps(lambda: fa.fa_bwd(*a, o2, l2, do2, w2.scale, True, dq=gq, dk=gk, dv=gv,
+                                           workspace=ws2), max(20, args.steps // 4), args.warmup,
+                         args.prewarm_ms)
+    wl["bwd_causal_mha"] = rate_entry(fb, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9)
+    wl["bwd_causal_mha"].update({"flops": fb, "kernels": "bwd_prep + bwd_dkdv + bwd_dq"})
+    del a, do2, o2, l2, gq, gk, gv, ws2, w2
+    torch.cuda.empty_cache()
+    if not all_workloads:
+        return wl
+    w3 = workloads.causal_gqa_long()
+    a = [t.cuda() for t in (w3.q, w3.k, w3.v)]
+    do3 = workloads.upstream_grad(1003, tuple(w3.q.shape)).cuda()
+    o3, l3 = fa.fa_fwd(*a, w3.scale, True)
+    ws3 = torch.empty(fa.fa_bwd_workspace_size(1, 32, 16384), dtype=torch.uint8, device="cuda")
+    g3 = [torch.empty_like(t) for t in a]
+    fb3 = 2.5 * dense_flops(w3)
+    _, dur = timed_steps(lambda: fa.fa_bwd(*a, o3, l3, do3, w3.scale, True, dq=g3[0], dk=g3[1],
+                                           dv=g3[2], workspace=ws3), 10, 2, args.prewarm_ms)
+    wl["bwd_causal_gqa_long"] = rate_entry(fb3, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9)
+    wl["bwd_causal_gqa_long"]["flops"] = fb3
+    del a, do3, o3, l3, ws3, g3, w3
+    torch.cuda.empty_cache()
+    w5 = workloads.varlen_window()
+    a = [t.cuda() for t in (w5.q, w5.k, w5.v)]
+    cu5 = torch.from_numpy(w5.cu_seqlens).cuda()
+    do5 = workloads.upstream_grad(1005, tuple(w5.q.shape)).cuda()
+    o5, l5 = fa.fa_fwd_varlen(*a, cu5, cu5, w5.max_seqlen, w5.max_seqlen, w5.scale, True,
+                              w5.window)
+    ws5 = torch.empty(fa.fa_bwd_varlen_workspace_size(len(w5.lens), 16, int(w5.cu_seqlens[-1])),
+                      dtype=torch.uint8, device="cuda")
+    g5 = [torch.empty_like(t) for t in a]
+    fb5 = 2.5 * varlen_flops(w5)
+    _, dur = timed_steps(lambda: fa.fa_bwd_varlen(*a, o5, l5, do5, cu5, cu5, w5.max_seqlen,
+                                                  w5.max_seqlen, w5.scale, True, w5.window,
+                                                  dq=g5[0], dk=g5[1], dv=g5[2], workspace=ws5),
+                         max(20, args.steps // 4), args.warmup, args.prewarm_ms)
+    wl["bwd_varlen_window"] = rate_entry(fb5, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9)
+    wl["bwd_varlen_window"]["flops"] = fb5
+    del a, cu5, do5, o5, l5, ws5, g5, w5
+    torch.cuda.empty_cache()
+    return wl
+
+
+def bench_small_and_chunked(fa, args):
+    wl = {}
+    w1 = workloads.small_dense(Hkv=1)
+    a = [t.cuda() for t in (w1.q, w1.k, w1.v)]
+    _, dur = timed_steps(lambda: fa.fa_fwd(*a, w1.scale, False), args.steps, args.warmup,
+                         args.prewarm_ms)
+    st = stats(dur)
+    wl["small_dense"] = {"ms": round(st["mean"], 4), "median_ms": round(st["median"], 4),
+                         "TFLOP/s": round(dense_flops(w1) / st["mean"] / 1e9, 3)}
+    del a
+    w6 = workloads.chunked_prefill()
+    q6, kc6, vc6 = w6.q.cuda(), w6.k_cache.cuda(), w6.v_cache.cuda()
+    kn6, vn6 = w6.k_new.cuda(), w6.v_new.cuda()
+    bt6 = torch.from_numpy(w6.block_table).cuda()
+    sl6 = torch.from_numpy(w6.cache_seqlens).cuda()
+    Lq6, Hq6, d6 = w6.q.shape[1], w6.q.shape[2], w6.q.shape[3]
+    f6 = 4.0 * d6 * Hq6 * sum(visible_pairs(Lq6, int(n) + Lq6, True, -1, -1) for n in w6.cache_seqlens)
+    # a step appends the chunk's K/V rows (same values each call) and attends over the cache
+    _, dur = timed_steps(lambda: fa.fa_fwd_kvcache(q6, kc6, vc6, bt6, sl6, kn6, vn6, w6.scale, True),
+                         args.steps, args.warmup, args.prewarm_ms)
+    wl["chunked_prefill"] = rate_entry(f6, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9)
+    wl["chunked_prefill"].update({"flops": f6, "kernels": "kvcache_append + prefill_fwd<paged>"})
+    del q6, kc6, vc6, kn6, vn6, w6
+    return wl
+
+
+def bench_decode(fa, args, extras):
+    """fa_decode_paged (the boundary call: no host plan) is the decode roofline;
+    the planned run and the 64-query-head variant are reported beside it."""
+    wl = {}
+    w4 = workloads.paged_decode()
+    qd, kc, vc = w4.q.cuda(), w4.k_cache.cuda(), w4.v_cache.cuda()
+    bt = torch.from_numpy(w4.block_table).cuda()
+    sl = torch.from_numpy(w4.seqlens).cuda()
+    ws = torch.empty(fa.fa_decode_paged_workspace_size(64, 32, 128, bt.shape[1], 16, 512),
+                     dtype=torch.uint8, device="cuda")
+    od = torch.empty_like(qd)
+    ld = torch.empty((64, 32), dtype=torch.float32, device="cuda")
+    nb = decode_bytes(w4)
+    kernels = "decode_order + decode_split_heads<128,4,nt> + decode_merge"
+    _, dur = timed_steps(lambda: fa.fa_decode_paged(qd, kc, vc, bt, sl, w4.scale, -1, 512, out=od,
+                                                    lse=ld, workspace=ws),
+                         args.steps, args.warmup, args.prewarm_ms)
+    wl["paged_decode"] = rate_entry(nb, dur, "GB/s", PEAK_HBM_GBS, 1e6)
+    wl["paged_decode"].update({"bytes": nb, "kernels": kernels})
+    roof = roofline_block("hbm", nb, dur, "GB/s", PEAK_HBM_GBS, 1e6,
+                          load_traffic("decode_paged_traffic", DECODE_SRC), kernels)
+    roof["workload"] = w4.name
+    if extras:
+        # plan / run split: the host plan lists only the (request, split) pairs that hold
+        # keys, heaviest first; made once per batch composition, its host time is
+        # reported beside the run (a decode loop remakes it whenever lengths change)
+        t0 = time.perf_counter()
+        plan = fa.fa_decode_plan(w4.seqlens, 16, bt.shape[1], -1, 512)
+        plan_ms = (time.perf_counter() - t0) * 1e3
+        plan_d = torch.from_numpy(plan).cuda()
+        _, dur = timed_steps(lambda: fa.fa_decode_paged_run(qd, kc, vc, bt, sl, plan_d, w4.scale,
+                                                            -1, 512, out=od, lse=ld, workspace=ws),
+                             args.steps, args.warmup, args.prewarm_ms)
+        e = rate_entry(nb, dur, "GB/s", PEAK_HBM_GBS, 1e6)
+        e.update({"bytes": nb, "plan_host_ms": round(plan_ms, 4), "plan_items": int(plan.shape[0]),
+                  "kernels": "decode_split_heads<128,4,nt> (planned) + decode_merge"})
+        e["GB/s_with_host_plan"] = round(nb / (e["ms"] + plan_ms) / 1e6, 1)
+        wl["paged_decode_planned"] = e
+        # the same cache and plan with 64 query heads (8 per KV head: two-KV-head sets)
+        q8 = workloads.device_normal(40, (64, 1, 64, 128))
+        o8, l8 = torch.empty_like(q8), torch.empty((64, 64), dtype=torch.float32, device="cuda")
+        ws8 = torch.empty(fa.fa_decode_paged_workspace_size(64, 64, 128, bt.shape[1], 16, 512),
+                          dtype=torch.uint8, device="cuda")
+        _, dur = timed_steps(lambda: fa.fa_decode_paged_run(q8, kc, vc, bt, sl, plan_d, w4.scale,
+                                                            -1, 512, out=o8, lse=l8, workspace=ws8),
+                             args.steps, args.warmup, args.prewarm_ms)
+        nb8 = nb + 2 * 64 * 32 * 128 * 2 + 64 * 32 * 4     # q, o and lse of the 32 more heads
+        e = rate_entry(nb8, dur, "GB/s", PEAK_HBM_GBS, 1e6)
+        e.update({"bytes": nb8, "kernels": "decode_split_heads<128,2> (planned) + decode_merge"})
+        wl["paged_decode_gqa8_planned"] = e
+        del q8, o8, l8, ws8, plan_d
+    del qd, kc, vc, w4
+    torch.cuda.empty_cache()
+    return wl, roof
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed back-to-back calls before the warmup steps of each workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only-main", action="store_true", help="time only the main workload")
-    ap.add_argument("--only-decode", action="store_true", help="time only the paged decode workload")
-    ap.add_argument("--only-bwd", action="store_true", help="time only the backward workload")
+    ap.add_argument("--only", choices=["main", "causal_mha", "varlen_window", "decode", "bwd"],
+                    help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain copy of known size (for byte-counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        print("bench.py: --steps must be at least 1", file=sys.stderr)
         sys.exit(2)
 
     import exact_attention_17_amd as fa
@@ -195,228 +501,27 @@ def main():
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
               "data": "synthetic", "device": props.name, "prewarm_ms": args.prewarm_ms}
-    w2 = workloads.causal_mha()
-    flops2 = dense_flops(w2)
-    if not args.only_decode and not args.only_bwd:
-        result.update(bench_main(fa, w2, flops2, args))
+    only = args.only
+    w3 = workloads.causal_gqa_long()
+    flops3 = dense_flops(w3)
     wl = {}
-    if args.only_bwd:
-        wl = bench_bwd(fa, args)
-    elif not args.only_main:
-        wl, roof_dec = bench_others(fa, args)
-        result["roofline_decode"] = roof_dec
+    if only in (None, "main"):
+        result.update(bench_main(fa, w3, flops3, args))
+    if only in (None, "causal_mha"):
+        wl["causal_mha"], result["roofline_causal_mha"] = bench_causal_mha(fa, args)
+    if only in (None, "varlen_window"):
+        wl.update(bench_varlen(fa, args))
+    if only in (None, "decode"):
+        dwl, result["roofline_decode"] = bench_decode(fa, args, extras=only is None)
+        wl.update(dwl)
+    if only in (None, "bwd"):
+        wl.update(bench_bwd(fa, args, all_workloads=only is None))
+    if only is None:
+        wl.update(bench_small_and_chunked(fa, args))
     result["workloads"] = wl
-    if not args.no_cpu_baseline and not args.only_decode and not args.only_bwd:
-        result["cpu_baseline"] = cpu_baseline(w2, flops2)
+    if not args.no_cpu_baseline and only in (None, "main"):
+        result["cpu_baseline"] = cpu_baseline(w3, flops3, per_workload=only is None)
     print(json.dumps(result), flush=True)
-
-
-def bench_main(fa, w2, flops2, args):
-    """The contract step: K timed fa_fwd calls on the causal MHA workload."""
-    q, k, v = w2.q.cuda(), w2.k.cuda(), w2.v.cuda()
-    o = torch.empty_like(q)
-    lse = torch.empty((4, 32, 2048), dtype=torch.float32, device="cuda")
-    step = lambda: fa.fa_fwd(q, k, v, w2.scale, True, (-1, -1), out=o, lse=lse)
-    prewarm(step, args.prewarm_ms)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    ev_ms = time_calls(step, args.steps, 2)
-    value = flops2 / (wall_ms * 1e-3) / 1e12
-    achieved = flops2 / (ev_ms * 1e-3) / 1e12
-    traffic = load_traffic("prefill_fwd_causal_mha_traffic", PREFILL_SRC)
-    return {
-        "value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(wall_ms, 4),
-        "config": {"workload": w2.name, "B": 4, "Hq": 32, "Hkv": 32, "L": 2048, "d": 128,
-                   "causal": True, "flops_per_step": flops2},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "prefill_fwd_kernel<128,false>",
-                     "avg_launch_ms": round(ev_ms, 4)},
-    }
-
-
-def bench_bwd(fa, args):
-    """Backward of the causal MHA workload: prep + dK/dV + dQ kernels; algorithmic
-    work = the five products of the chain rule (S, dP, dV, dK, dQ), 2.5x the forward."""
-    wl = {}
-    w2 = workloads.causal_mha()
-    a = [t.cuda() for t in (w2.q, w2.k, w2.v)]
-    do2 = workloads.upstream_grad(1002, tuple(w2.q.shape)).cuda()
-    o2, l2 = fa.fa_fwd(*a, w2.scale, True)
-    gq, gk, gv = torch.empty_like(a[0]), torch.empty_like(a[1]), torch.empty_like(a[2])
-    ws2 = torch.empty(fa.fa_bwd_workspace_size(4, 32, 2048), dtype=torch.uint8, device="cuda")
-    fb = 2.5 * dense_flops(w2)
-    ms = time_calls(lambda: fa.fa_bwd(*a, o2, l2, do2, w2.scale, True, dq=gq, dk=gk, dv=gv,
-                                      workspace=ws2), max(20, args.steps // 4), args.warmup,
-                    args.prewarm_ms)
-    wl["bwd_causal_mha"] = {"ms": round(ms, 4), "TFLOP/s": round(fb / ms / 1e9, 2),
-                            "frac_mfma": round(fb / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": fb,
-                            "kernels": "bwd_prep + bwd_dkdv + bwd_dq"}
-    del a, do2, o2, l2, gq, gk, gv, ws2, w2
-    torch.cuda.empty_cache()
-    if not args.only_bwd:
-        # long-context GQA backward (B=1, Hq=32, Hkv=8, L=16384): dK, dV of a KV
-        # head sum its 4 query heads inside one workgroup
-        w3 = workloads.causal_gqa_long()
-        a = [t.cuda() for t in (w3.q, w3.k, w3.v)]
-        do3 = workloads.upstream_grad(1003, tuple(w3.q.shape)).cuda()
-        o3, l3 = fa.fa_fwd(*a, w3.scale, True)
-        ws3 = torch.empty(fa.fa_bwd_workspace_size(1, 32, 16384), dtype=torch.uint8, device="cuda")
-        g3 = [torch.empty_like(t) for t in a]
-        fb3 = 2.5 * dense_flops(w3)
-        ms = time_calls(lambda: fa.fa_bwd(*a, o3, l3, do3, w3.scale, True, dq=g3[0], dk=g3[1],
-                                          dv=g3[2], workspace=ws3), 5, 2, args.prewarm_ms)
-        wl["bwd_causal_gqa_long"] = {"ms": round(ms, 4), "TFLOP/s": round(fb3 / ms / 1e9, 2),
-                                     "frac_mfma": round(fb3 / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                     "flops": fb3}
-        del a, do3, o3, l3, ws3, g3, w3
-        torch.cuda.empty_cache()
-        # varlen + sliding-window backward (the varlen window workload, d = 64)
-        w5 = workloads.varlen_window()
-        a = [t.cuda() for t in (w5.q, w5.k, w5.v)]
-        cu5 = torch.from_numpy(w5.cu_seqlens).cuda()
-        do5 = workloads.upstream_grad(1005, tuple(w5.q.shape)).cuda()
-        o5, l5 = fa.fa_fwd_varlen(*a, cu5, cu5, w5.max_seqlen, w5.max_seqlen, w5.scale, True,
-                                  w5.window)
-        ws5 = torch.empty(fa.fa_bwd_varlen_workspace_size(len(w5.lens), 16, int(w5.cu_seqlens[-1])),
-                          dtype=torch.uint8, device="cuda")
-        g5 = [torch.empty_like(t) for t in a]
-        fb5 = 2.5 * varlen_flops(w5)
-        ms = time_calls(lambda: fa.fa_bwd_varlen(*a, o5, l5, do5, cu5, cu5, w5.max_seqlen,
-                                                 w5.max_seqlen, w5.scale, True, w5.window,
-                                                 dq=g5[0], dk=g5[1], dv=g5[2], workspace=ws5),
-                        max(20, args.steps // 4), args.warmup, args.prewarm_ms)
-        wl["bwd_varlen_window"] = {"ms": round(ms, 4), "TFLOP/s": round(fb5 / ms / 1e9, 2),
-                                   "frac_mfma": round(fb5 / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                   "flops": fb5}
-        del a, cu5, do5, o5, l5, ws5, g5, w5
-        torch.cuda.empty_cache()
-    return wl
-
-
-def bench_others(fa, args):
-    """Time the remaining workloads; returns (per-workload dict, decode roofline)."""
-    wl = {}
-    if not args.only_decode:
-        w1 = workloads.small_dense(Hkv=1)
-        a = [t.cuda() for t in (w1.q, w1.k, w1.v)]
-        ms = time_calls(lambda: fa.fa_fwd(*a, w1.scale, False), args.steps, args.warmup, args.prewarm_ms)
-        wl["small_dense"] = {"ms": round(ms, 4), "TFLOP/s": round(dense_flops(w1) / ms / 1e9, 3)}
-        del a
-
-        wl.update(bench_bwd(fa, args))
-
-        w3 = workloads.causal_gqa_long()
-        a = [t.cuda() for t in (w3.q, w3.k, w3.v)]
-        f3 = dense_flops(w3)
-        ms = time_calls(lambda: fa.fa_fwd(*a, w3.scale, True), max(5, args.steps // 10), 3, args.prewarm_ms)
-        wl["causal_gqa_long"] = {"ms": round(ms, 4), "TFLOP/s": round(f3 / ms / 1e9, 2),
-                                 "frac_mfma": round(f3 / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                 "flops": f3}
-        del a, w3
-
-        w5 = workloads.varlen_window()
-        a = [t.cuda() for t in (w5.q, w5.k, w5.v)]
-        cu = torch.from_numpy(w5.cu_seqlens).cuda()
-        f5 = varlen_flops(w5)
-        ms = time_calls(lambda: fa.fa_fwd_varlen(*a, cu, cu, w5.max_seqlen, w5.max_seqlen, w5.scale,
-                                                 True, w5.window), args.steps, args.warmup,
-                        args.prewarm_ms)
-        wl["varlen_window"] = {"ms": round(ms, 4), "TFLOP/s": round(f5 / ms / 1e9, 2),
-                               "frac_mfma": round(f5 / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": f5}
-        # plan / run split: the host plan (heaviest tiles first) is made once for the
-        # batch's lengths and reused; its host time is reported beside the run
-        t0 = time.perf_counter()
-        plan = fa.fa_varlen_plan(w5.cu_seqlens, w5.cu_seqlens, True, w5.window)
-        plan_ms = (time.perf_counter() - t0) * 1e3
-        plan_d = torch.from_numpy(plan).cuda()
-        ms = time_calls(lambda: fa.fa_fwd_varlen_run(*a, cu, cu, plan_d, w5.max_seqlen,
-                                                     w5.max_seqlen, w5.scale, True, w5.window),
-                        args.steps, args.warmup, args.prewarm_ms)
-        wl["varlen_window_planned"] = {"ms": round(ms, 4), "TFLOP/s": round(f5 / ms / 1e9, 2),
-                                       "frac_mfma": round(f5 / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                       "flops": f5, "plan_host_ms": round(plan_ms, 4),
-                                       "plan_items": int(plan.shape[0])}
-        del a, w5, plan_d
-
-        w6 = workloads.chunked_prefill()
-        q6, kc6, vc6 = w6.q.cuda(), w6.k_cache.cuda(), w6.v_cache.cuda()
-        kn6, vn6 = w6.k_new.cuda(), w6.v_new.cuda()
-        bt6 = torch.from_numpy(w6.block_table).cuda()
-        sl6 = torch.from_numpy(w6.cache_seqlens).cuda()
-        Lq6, Hq6, d6 = w6.q.shape[1], w6.q.shape[2], w6.q.shape[3]
-        f6 = 4.0 * d6 * Hq6 * sum(visible_pairs(Lq6, int(n) + Lq6, True, -1, -1) for n in w6.cache_seqlens)
-        # a step appends the chunk's K/V rows (same values each call) and attends over the cache
-        ms = time_calls(lambda: fa.fa_fwd_kvcache(q6, kc6, vc6, bt6, sl6, kn6, vn6, w6.scale, True),
-                        args.steps, args.warmup, args.prewarm_ms)
-        wl["chunked_prefill"] = {"ms": round(ms, 4), "TFLOP/s": round(f6 / ms / 1e9, 2),
-                                 "frac_mfma": round(f6 / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": f6,
-                                 "kernels": "kvcache_append + prefill_fwd<paged>"}
-        del q6, kc6, vc6, kn6, vn6, w6
-
-    w4 = workloads.paged_decode()
-    qd, kc, vc = w4.q.cuda(), w4.k_cache.cuda(), w4.v_cache.cuda()
-    bt = torch.from_numpy(w4.block_table).cuda()
-    sl = torch.from_numpy(w4.seqlens).cuda()
-    ws = torch.empty(fa.fa_decode_paged_workspace_size(64, 32, 128, bt.shape[1], 16, 512),
-                     dtype=torch.uint8, device="cuda")
-    od = torch.empty_like(qd)
-    ld = torch.empty((64, 32), dtype=torch.float32, device="cuda")
-    nb = decode_bytes(w4)
-    if not args.only_decode:
-        # every (split slot, request) launched; slots past a request's length exit at once
-        ms = time_calls(lambda: fa.fa_decode_paged(qd, kc, vc, bt, sl, w4.scale, -1, 512, out=od,
-                                                   lse=ld, workspace=ws), args.steps,
-                        args.warmup, args.prewarm_ms)
-        gbs = nb / ms / 1e6
-        wl["paged_decode"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
-                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb,
-                              "kernels": "decode_order + decode_split_heads<128,4,nt> (device-made order) + decode_merge"}
-    # plan / run split: the host plan lists only the (request, split) pairs that hold
-    # keys, heaviest first; it is made once for the batch's lengths and its host time
-    # is reported beside the run.  The decode roofline is this run's.
-    t0 = time.perf_counter()
-    plan = fa.fa_decode_plan(w4.seqlens, 16, bt.shape[1], -1, 512)
-    plan_ms = (time.perf_counter() - t0) * 1e3
-    plan_d = torch.from_numpy(plan).cuda()
-    ms = time_calls(lambda: fa.fa_decode_paged_run(qd, kc, vc, bt, sl, plan_d, w4.scale, -1, 512,
-                                                   out=od, lse=ld, workspace=ws),
-                    args.steps, args.warmup, args.prewarm_ms)
-    gbs = nb / ms / 1e6
-    wl["paged_decode_planned"] = {"ms": round(ms, 4), "GB/s": round(gbs, 1),
-                                  "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nb,
-                                  "plan_host_ms": round(plan_ms, 4),
-                                  "plan_items": int(plan.shape[0]),
-                                  "kernels": "decode_split_heads<128,4,nt> (planned) + decode_merge"}
-    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic("decode_paged_traffic", DECODE_SRC),
-            "kernel": "decode_split_heads<128,4,nt> (planned) + decode_merge", "avg_launch_ms": round(ms, 4)}
-    if not args.only_decode:
-        # the same cache and plan with 64 query heads (8 per KV head: two-KV-head sets);
-        # not a bench line of its own, reported beside it
-        q8 = workloads.device_normal(40, (64, 1, 64, 128))
-        o8, l8 = torch.empty_like(q8), torch.empty((64, 64), dtype=torch.float32, device="cuda")
-        ws8 = torch.empty(fa.fa_decode_paged_workspace_size(64, 64, 128, bt.shape[1], 16, 512),
-                          dtype=torch.uint8, device="cuda")
-        ms8 = time_calls(lambda: fa.fa_decode_paged_run(q8, kc, vc, bt, sl, plan_d, w4.scale, -1, 512,
-                                                        out=o8, lse=l8, workspace=ws8),
-                         args.steps, args.warmup, args.prewarm_ms)
-        nb8 = nb + 2 * 64 * 32 * 128 * 2 + 64 * 32 * 4     # q, o and lse of the 32 more heads
-        gbs8 = nb8 / ms8 / 1e6
-        wl["paged_decode_gqa8_planned"] = {"ms": round(ms8, 4), "GB/s": round(gbs8, 1),
-                                           "frac_hbm": round(gbs8 / PEAK_HBM_GBS, 4), "bytes": nb8,
-                                           "kernels": "decode_split_heads<128,2> (planned) + decode_merge"}
-        del q8, o8, l8, ws8
-    del qd, kc, vc, w4, plan_d
-    torch.cuda.empty_cache()
-    return wl, roof
 
 
 if __name__ == "__main__":
