@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["fa_api.cpp", "plan.cpp", "prefill_fwd.hip", "decode_paged.hip", "attn_bwd.hip"]
+SOURCES = ["fa_api.cpp", "plan.cpp", "prefill_fwd.hip", "prefill_wide.hip", "decode_paged.hip",
+           "attn_bwd.hip"]
 ARCH = "gfx950"
 
 

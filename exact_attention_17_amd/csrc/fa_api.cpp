@@ -111,12 +111,21 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.scale_log2 = softmax_scale * kLog2e;
   p.causal = causal; p.win_left = norm_window(window_left); p.win_right = norm_window(window_right);
   set_mods(p, softmax_scale, softcap, alibi_slopes, alibi_batch_stride);
-  p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
+  // Long sequences at head_dim 128 take the wide-tile kernel (256 query rows,
+  // one workgroup per CU): its steady state is faster, but a workgroup's fixed
+  // start and end cost is not hidden by a second workgroup on the CU, which
+  // outweighs that below a few thousand query rows.  Everything else takes the
+  // narrow kernel (128 rows; two workgroups per CU at head_dim 128, three at 64).
+  const bool wide = d == 128 && Lq >= fa::kWideMinRows;
+  const int rows = wide ? fa::kWideRows : fa::kBlockM;
+  const int slots = wide ? fa::kWideSlotsPerXcd : fa::kPrefillSlotsPerXcd;
+  p.num_q_tiles = (int)cdiv(Lq, rows);
   p.xcd_groups = xcd_groups(B * Hkv);
   // KV groups per XCD chunk: about one XCD's worth of resident workgroups
-  p.chunk_groups = (int)std::max<int64_t>(1, fa::kPrefillSlotsPerXcd / ((int64_t)p.group * p.num_q_tiles));
+  p.chunk_groups = (int)std::max<int64_t>(1, slots / ((int64_t)p.group * p.num_q_tiles));
   if ((int64_t)p.num_q_tiles * B * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
-  hipError_t e = fa::launch_prefill(p, d, 0, static_cast<hipStream_t>(stream));
+  hipError_t e = wide ? fa::launch_prefill_wide(p, static_cast<hipStream_t>(stream))
+                      : fa::launch_prefill(p, d, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

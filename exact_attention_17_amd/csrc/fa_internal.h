@@ -19,6 +19,11 @@ constexpr int kDecodeChunk = 64;     // keys per wave iteration
 constexpr int kDefaultSplit = 512;
 // Prefill workgroups resident per XCD (32 CUs x 2), used to size work chunks.
 constexpr int kPrefillSlotsPerXcd = 64;
+// Wide-tile prefill (head_dim 128, dense): 256 query rows per workgroup, one
+// workgroup per CU.
+constexpr int kWideRows = 256;
+constexpr int kWideSlotsPerXcd = 32;
+constexpr int kWideMinRows = 4096;   // query rows from which fa_fwd takes it
 
 struct PrefillParams {
   const uint16_t* q;       // bf16 bits
@@ -127,6 +132,8 @@ struct DecodeParams {
 
 // mode: 0 dense, 1 varlen, 2 paged KV cache
 hipError_t launch_prefill(const PrefillParams& p, int d, int mode, hipStream_t stream);
+// dense, head_dim 128; p.num_q_tiles and p.chunk_groups sized for kWideRows
+hipError_t launch_prefill_wide(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, int rows, hipStream_t stream);
 // row statistics, then dK/dV, then dQ, in stream order

@@ -586,3 +586,57 @@ def test_decode_many_requests(fa, Hq, Hkv, d):
     check(f"decode many requests h{Hq} kv{Hkv} d{d}", o, lse, O, LSE)
     o2, lse2 = run_decode_planned(fa, w)
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+
+
+# ------------------------------------------------ wide-tile kernel (d = 128)
+# fa_fwd takes the 256-row wide-tile kernel for head_dim 128 from 4096 query
+# rows on; these cases sit just past that, with ragged 256-row and 64-key
+# tails, so every mask mode, GQA, Lq != Lk, the rescale paths and the score
+# modifiers run through it (the smaller dense cases above take the narrow one).
+WIDE_CASES = [
+    # B, Lq, Lk, Hq, Hkv, causal, window, softcap, alibi
+    (1, 4133, 4133, 2, 1, True, (-1, -1), 0.0, "none"),
+    (1, 4096, 4096, 2, 2, False, (-1, -1), 0.0, "none"),
+    (1, 4100, 4500, 2, 1, True, (-1, -1), 0.0, "none"),     # Lq < Lk: bottom-right causal
+    (1, 4500, 4100, 2, 2, True, (-1, -1), 0.0, "none"),     # Lq > Lk: first 400 rows see no key
+    (1, 4111, 4111, 4, 2, True, (300, 0), 0.0, "none"),     # sliding window
+    (1, 4099, 4099, 2, 1, False, (200, 37), 0.0, "none"),   # two-sided window
+    (2, 4097, 4097, 2, 1, True, (-1, -1), 20.0, "head"),    # softcap + ALiBi
+    (1, 4160, 4160, 2, 2, True, (64, 0), 0.0, "batch"),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: f"L{c[1]}x{c[2]}-h{c[3]}_{c[4]}-c{int(c[5])}-w{c[6][0]}_{c[6][1]}-cap{c[7]}-{c[8]}")
+def test_wide_kernel_sweep(fa, case):
+    B, Lq, Lk, Hq, Hkv, causal, window, cap, al = case
+    w = workloads.random_dense(900 + Lq + Lk + Hq, B, Lq, Lk, Hq, Hkv, 128, causal, window)
+    slopes = None if al == "none" else alibi_slopes(Hq, B if al == "batch" else None)
+    q = dev(w.q)
+    out = nan_like(q)
+    lse = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device="cuda")
+    o, l = fa.fa_fwd(q, dev(w.k), dev(w.v), w.scale, causal, window, out=out, lse=lse, softcap=cap,
+                     alibi_slopes=None if slopes is None else dev(torch.from_numpy(slopes)))
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_ref(bits(w.q), bits(w.k), bits(w.v), w.scale, causal, window,
+                                  softcap=cap, alibi_slopes=slopes)
+    check(f"wide{case}", o.cpu(), l.cpu(), O, LSE)
+
+
+@pytest.mark.parametrize("kind", ["rising", "large_scale"])
+def test_wide_kernel_rescale_paths(fa, kind):
+    """Scores that rise along the keys (the max is raised on many tiles, through
+    both the up-front and the after-the-block paths), and a large scale that
+    makes P nearly one-hot, through the wide-tile kernel."""
+    B, L, H = 1, 4200, 2
+    if kind == "rising":
+        w = workloads.random_dense(77, B, L, L, H, H, 128, True)
+        k = w.k.float()
+        qdir = w.q.float()[:, -1:, :, :] / w.q.float()[:, -1:, :, :].norm(dim=-1, keepdim=True)
+        w.k = (k + torch.linspace(0, 40, L).view(1, L, 1, 1) * qdir).to(torch.bfloat16)
+        scale = w.scale
+    else:
+        w = workloads.random_dense(78, B, L, L, H, 1, 128, True, scale=2.0)
+        scale = 2.0
+    o, lse = run_dense(fa, w)
+    O, LSE = oracle.attention_ref(bits(w.q), bits(w.k), bits(w.v), scale, True)
+    check(f"wide_{kind}", o, lse, O, LSE)
