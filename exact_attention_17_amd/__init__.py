@@ -61,6 +61,9 @@ _EXPORTS = {
     "fa_decode_paged": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 2
                         + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int] + _MODS
                         + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fa_decode_paged_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 2
+                                + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int] + _MODS
+                                + [ctypes.c_int, ctypes.c_void_p]),
     "fa_fwd_kvcache": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 8
                        + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int]
                        + _MODS + [ctypes.c_void_p]),
@@ -377,6 +380,37 @@ def fa_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, softmax_sca
     return out, lse
 
 
+DECODE_NOALLOC_MAX_BYTES = 32 << 20
+
+
+def fa_decode_paged_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale=None,
+                            window_left=-1, split_tokens=0, out=None, lse=None, return_lse=True,
+                            stream=None, softcap=0.0, alibi_slopes=None):
+    """fa_decode_paged without a workspace: the library's per-GPU scratch array
+    (DECODE_NOALLOC_MAX_BYTES) holds the split partials.  Pass out (and lse) to make
+    the call allocate nothing at all; calls that can overlap on one GPU must be
+    ordered by the caller (they share the array)."""
+    torch = _torch()
+    lib = load_library()
+    num_pages, page_size, Hkv = _paged_inputs(q, k_cache, v_cache, block_table, cache_seqlens)
+    B, one, Hq, d = q.shape
+    if one != 1:
+        raise ValueError("q must be (B, 1, Hq, d)")
+    dev = q.device
+    s = _stream_obj(stream)
+    out = _output(out, "out", (B, 1, Hq, d), torch.bfloat16, dev, s)
+    if return_lse or lse is not None:
+        lse = _output(lse, "lse", (B, Hq), torch.float32, dev, s)
+    mods = _mods(softcap, alibi_slopes, B, Hq, dev)
+    st = lib.fa_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                     _ptr(cache_seqlens), _ptr(out), _ptr(lse), B, Hq, Hkv, d,
+                                     num_pages, page_size, block_table.shape[1],
+                                     _scale(softmax_scale, d), int(window_left), *mods,
+                                     int(split_tokens), _stream(s))
+    _check("fa_decode_paged_noalloc", st)
+    return out, lse
+
+
 def fa_decode_plan(cache_seqlens, page_size, max_blocks_per_seq, window_left=-1, split_tokens=0):
     """Host plan for fa_decode_paged_run from HOST lengths (list, numpy array or CPU tensor of
     B ints) -> numpy int32 array (num_items, 2) of (request, split), heaviest first.  No GPU is
@@ -532,7 +566,8 @@ def fa_fwd_kvcache(q, k_cache, v_cache, block_table, cache_seqlens, k_new=None, 
 
 
 __all__ = ["fa_fwd", "fa_fwd_varlen", "fa_varlen_plan", "fa_fwd_varlen_run",
-           "fa_decode_paged", "fa_decode_plan", "fa_decode_paged_run",
+           "fa_decode_paged", "fa_decode_plan", "fa_decode_paged_run", "fa_decode_paged_noalloc",
+           "DECODE_NOALLOC_MAX_BYTES",
            "fa_decode_paged_workspace_size", "fa_fwd_kvcache", "fa_bwd",
            "fa_bwd_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
            "load_library", "exported_symbols", "cu_seqlens_from_lengths",

@@ -44,6 +44,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace fa {
 
 // Request b's key count, clamped to [0, max_blocks * page_size] (the block
@@ -863,6 +865,38 @@ static hipError_t launch_decode_d(const DecodeParams& p_in, int rows, hipStream_
 
 hipError_t launch_decode(const DecodeParams& p, int d, int rows, hipStream_t stream) {
   return d == 128 ? launch_decode_d<128>(p, rows, stream) : launch_decode_d<64>(p, rows, stream);
+}
+
+// Device memory of the allocation-free decode call (fa_decode_paged_noalloc):
+// the split partials and the work order live here instead of in a caller's
+// workspace.  Each GPU the library runs on holds one copy for the life of the
+// process; host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device (the array's own name is not a device
+// address in host code).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+void* decode_scratch(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  *err = hipSuccess;
+  return ptrs[dev];
 }
 
 }  // namespace fa

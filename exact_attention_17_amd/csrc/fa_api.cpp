@@ -9,6 +9,9 @@
 
 #include <algorithm>
 
+static_assert(FA_DECODE_NOALLOC_MAX_BYTES == fa::kDecodeScratchBytes,
+              "the header's scratch limit must match the array's size");
+
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
@@ -422,6 +425,32 @@ fa_status fa_decode_paged_run(const void* q, const void* k_cache, const void* v_
                      Hq, Hkv, d, num_pages, page_size, max_blocks_per_seq, softmax_scale,
                      window_left, softcap, alibi_slopes, alibi_batch_stride, split_tokens,
                      workspace, workspace_bytes, stream);
+}
+
+fa_status fa_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int* block_table, const int* cache_seqlens,
+                                  void* o, float* lse, int B, int Hq, int Hkv, int d,
+                                  int num_pages, int page_size, int max_blocks_per_seq,
+                                  float softmax_scale, int window_left, float softcap,
+                                  const float* alibi_slopes, int alibi_batch_stride,
+                                  int split_tokens, void* stream) {
+  // every argument check of fa_decode_paged, without a workspace: it reports
+  // the missing workspace only when all else is valid (no HIP call is made)
+  fa_status st = decode_impl(q, k_cache, v_cache, block_table, cache_seqlens, false, nullptr, 0, o,
+                             lse, B, Hq, Hkv, d, num_pages, page_size, max_blocks_per_seq,
+                             softmax_scale, window_left, softcap, alibi_slopes, alibi_batch_stride,
+                             split_tokens, nullptr, 0, stream);
+  if (st != FA_ERR_WORKSPACE) return st;
+  const size_t need = fa_decode_paged_workspace_size(B, Hq, d, max_blocks_per_seq, page_size,
+                                                     split_tokens);
+  if (need > fa::kDecodeScratchBytes) return FA_ERR_WORKSPACE;
+  hipError_t e = hipSuccess;
+  void* scratch = fa::decode_scratch(&e);
+  if (!scratch) return FA_ERR_HIP;
+  return decode_impl(q, k_cache, v_cache, block_table, cache_seqlens, false, nullptr, 0, o, lse, B,
+                     Hq, Hkv, d, num_pages, page_size, max_blocks_per_seq, softmax_scale,
+                     window_left, softcap, alibi_slopes, alibi_batch_stride, split_tokens,
+                     scratch, fa::kDecodeScratchBytes, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Lq) {

@@ -136,6 +136,11 @@ hipError_t launch_prefill(const PrefillParams& p, int d, int mode, hipStream_t s
 hipError_t launch_prefill_wide(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, int rows, hipStream_t stream);
+// Size of the device scratch array behind fa_decode_paged_noalloc, and its
+// address on the current device (looked up once per device); NULL and *err set
+// if the lookup fails.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+void* decode_scratch(hipError_t* err);
 // row statistics, then dK/dV, then dQ, in stream order
 hipError_t launch_bwd(const BwdParams& p, int d, bool varlen, hipStream_t stream);
 

@@ -51,7 +51,8 @@
  *     (monotone cu_seqlens ending at total, block_table entries in
  *     [0, num_pages) for the pages a request uses, cache_seqlens[b] <=
  *     max_blocks_per_seq * page_size) are the caller's responsibility.
- *   - Calls are reentrant and thread-safe: the library has no global state.
+ *   - Calls are reentrant and thread-safe: the library has no global state,
+ *     except the per-GPU scratch array of fa_decode_paged_noalloc (see there).
  */
 #ifndef FA_H
 #define FA_H
@@ -239,6 +240,39 @@ fa_status fa_decode_paged_run(const void* q, const void* k_cache, const void* v_
                               const float* alibi_slopes, int alibi_batch_stride,
                               int split_tokens, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * fa_decode_paged without a workspace, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation.  It computes exactly what
+ * fa_decode_paged computes (same kernels, bit for bit) and takes the same
+ * arguments minus workspace and workspace_bytes.  The split partials and the
+ * work order live instead in a device array of FA_DECODE_NOALLOC_MAX_BYTES
+ * (32 MiB) inside the library, one per GPU, reserved when the library is
+ * loaded on that GPU and held until the process ends; the call makes no
+ * allocation of any kind.
+ *   - A call needing more than that, i.e. fa_decode_paged_workspace_size(B,
+ *     Hq, d, max_blocks_per_seq, page_size, split_tokens) >
+ *     FA_DECODE_NOALLOC_MAX_BYTES, returns FA_ERR_WORKSPACE and enqueues
+ *     nothing (for example 64 requests x 32 query heads x d 128 x 8192-token
+ *     tables with 512-token splits need about 17 MiB).
+ *   - The first call on each GPU (with that GPU current) looks up the array's
+ *     device address (hipGetSymbolAddress); a failed lookup returns
+ *     FA_ERR_HIP.  Nothing in the array needs to start zeroed: every byte a
+ *     call reads, the same call wrote first.
+ *   - Every call on one GPU shares that GPU's array: calls that can overlap
+ *     on one GPU (different streams, or host threads) race and must be
+ *     ordered by the caller, e.g. by issuing them on one stream.  This is the
+ *     library's only global state.
+ */
+#define FA_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+fa_status fa_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int* block_table, const int* cache_seqlens,
+                                  void* o, float* lse, int B, int Hq, int Hkv, int d,
+                                  int num_pages, int page_size, int max_blocks_per_seq,
+                                  float softmax_scale, int window_left, float softcap,
+                                  const float* alibi_slopes, int alibi_batch_stride,
+                                  int split_tokens, void* stream);
 
 /*
  * Attention of Lq new query tokens per request over a paged KV cache

@@ -37,6 +37,7 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["fa_status_string", "fa_fwd", "fa_fwd_varlen", "fa_varlen_plan",
                             "fa_fwd_varlen_run", "fa_decode_paged_workspace_size",
                             "fa_decode_paged", "fa_decode_plan", "fa_decode_paged_run",
+                            "fa_decode_paged_noalloc",
                             "fa_fwd_kvcache", "fa_bwd", "fa_bwd_workspace_size",
                             "fa_bwd_varlen", "fa_bwd_varlen_workspace_size"])
     for n in names:
@@ -160,6 +161,37 @@ def decode(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
+
+
+def decode_noalloc(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, bt=P, sl=P, o=P, lse=P, B=4, Hq=8, Hkv=2, d=128, pages=64, ps=16,
+             mb=8, scale=0.1, wl=-1, cap=0.0, al=None, ast=0, split=0)
+    a.update(kw)
+    return lib.fa_decode_paged_noalloc(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["o"], a["lse"],
+                                       a["B"], a["Hq"], a["Hkv"], a["d"], a["pages"], a["ps"],
+                                       a["mb"], a["scale"], a["wl"], a["cap"], a["al"], a["ast"],
+                                       a["split"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), INVALID), (dict(sl=P + 1), INVALID), (dict(kc=None), INVALID),
+    (dict(pages=0), INVALID), (dict(split=24), INVALID), (dict(d=32), UNSUPPORTED),
+    (dict(Hkv=3), INVALID), (dict(cap=-1.0), INVALID),
+    # partials beyond the 32 MiB scratch array: 256 requests x 64 heads x 16 splits x 128 x 4 B
+    (dict(B=256, Hq=64, Hkv=8, mb=512), WORKSPACE),
+    (dict(B=64, Hq=32, Hkv=8, mb=512, split=16), WORKSPACE),
+])
+def test_decode_noalloc_rejects_before_any_hip_call(lib, kw, code):
+    assert decode_noalloc(lib, **kw) == code
+
+
+def test_decode_noalloc_limit_matches_workspace_size(lib):
+    """The 32 MiB scratch array holds the paged-decode workload's partials (64
+    requests, 32 query heads, 8192-token tables, 512-token splits) with room."""
+    assert fa.DECODE_NOALLOC_MAX_BYTES == 32 << 20
+    need = lib.fa_decode_paged_workspace_size(64, 32, 128, 512, 16, 512)
+    assert 0 < need <= fa.DECODE_NOALLOC_MAX_BYTES
+    assert lib.fa_decode_paged_workspace_size(256, 64, 128, 512, 16, 512) > fa.DECODE_NOALLOC_MAX_BYTES
 
 
 def decode_run(lib, **kw):
