@@ -50,7 +50,7 @@ namespace fa {
 
 // Request b's key count, clamped to [0, max_blocks * page_size] (the block
 // table's capacity); every decode kernel reads lengths through this.
-FA_DEV inline int clamp_len(const DecodeParams& p, int b) {
+FA_DEV int clamp_len(const DecodeParams& p, int b) {
   return (int)min((int64_t)max(p.seqlens[b], 0), (int64_t)p.max_blocks * p.page_size);
 }
 
