@@ -69,6 +69,123 @@ __device__ __forceinline__ float modify_score(const DecodeParams& p, float s, fl
     s = p.cap_out * (1.f - 2.f * __builtin_amdgcn_rcpf(exp2_fast(s * (2.f * kLog2eF * p.cap_in)) + 1.f));
   return s - slope * (float)dist;
 }
+
+// ---- the unplanned call's work order ---------------------------------------
+// Work items are the (request, split) pairs that hold a visible key: first
+// the full splits (split_tokens keys), request by request, then the partial
+// ones (a request's first split under a window, its last split), by size,
+// largest first, in 64 size buckets.  Small splits go last, so the launch's
+// tail is short.  Either one workgroup writes the whole list
+// (decode_order_kernel) or, for batches of at most kSelfOrderMaxB requests,
+// every workgroup of the head-set kernel finds its own slot's item
+// (self_order_item); there, within a bucket, partial splits are taken in
+// (request, split) order.  Results do not depend on the order.
+constexpr int kOrderBuckets = 64;
+constexpr int kSelfOrderMaxB = 256;
+
+FA_DEV int size_bucket(int keys, int S) { return (int)(((int64_t)keys * kOrderBuckets - 1) / S); }
+
+// Splits s0..s1 hold request b's visible keys [lo, len).  pf / pl: the size
+// bucket of its first / last split if that split is partial, else -1 (a
+// single partial split is its first); its full splits are ff..ff+nf-1.
+struct RequestSplits {
+  int s0, s1, ff, nf, pf, pl;
+};
+FA_DEV RequestSplits request_splits(const DecodeParams& p, int b) {
+  const int S = p.split_tokens;
+  const int len = clamp_len(p, b);
+  const int lo = p.win_left >= 0 ? max(0, len - 1 - p.win_left) : 0;
+  RequestSplits r;
+  r.s0 = lo / S;
+  r.s1 = len > 0 ? (len - 1) / S : r.s0 - 1;
+  r.ff = r.s0;
+  r.nf = 0;
+  r.pf = r.pl = -1;
+  if (r.s1 < r.s0) return r;
+  const int kf = min(len, r.s0 * S + S) - max(r.s0 * S, lo);
+  if (kf < S) {
+    r.pf = size_bucket(kf, S);
+    r.ff = r.s0 + 1;
+  }
+  if (r.s1 > r.s0 && len - r.s1 * S < S) r.pl = size_bucket(len - r.s1 * S, S);
+  r.nf = r.s1 - r.ff + 1 - (r.pl >= 0 ? 1 : 0);
+  return r;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+FA_DEV int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Item `item` of the order above, computed by one wave (every wave of a
+// workgroup gets the same answer): false if the slot holds no item.  hist:
+// 64 ints of the wave's own LDS.  Lanes take requests 64 at a time: full
+// splits by a prefix sum of their counts; a partial one by a histogram of the
+// buckets (lane j holds bucket 63 - j, so the prefix sum runs largest first),
+// then by a prefix sum over the requests of its bucket.
+FA_DEV bool self_order_item(const DecodeParams& p, int item, int* hist, int& b_out, int& s_out) {
+  const int lane = threadIdx.x & 63;
+  int base = 0, parts = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    RequestSplits r{0, -1, 0, 0, -1, -1};
+    if (c + lane < p.B) r = request_splits(p, c + lane);
+    const int incl = wave_incl_scan(r.nf);
+    const int tot = __shfl(incl, 63, 64);
+    parts += __shfl(wave_incl_scan((r.pf >= 0) + (r.pl >= 0)), 63, 64);
+    if (item < base + tot) {
+      const int rel = item - base;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(rel >= incl - r.nf && rel < incl);
+      const int src = (int)__builtin_ctzll(hit);
+      b_out = c + src;
+      s_out = __shfl(r.ff + rel - (incl - r.nf), src, 64);
+      return true;
+    }
+    base += tot;
+  }
+  int rank = item - base;            // among the partial splits
+  if (rank >= parts) return false;
+  hist[lane] = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    if (c + lane < p.B) {
+      const RequestSplits r = request_splits(p, c + lane);
+      if (r.pf >= 0) atomicAdd(&hist[r.pf], 1);
+      if (r.pl >= 0) atomicAdd(&hist[r.pl], 1);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int cnt = hist[63 - lane];
+  const int incl_b = wave_incl_scan(cnt);
+  const uint64_t hit_b = __builtin_amdgcn_ballot_w64(rank >= incl_b - cnt && rank < incl_b);
+  const int j = (int)__builtin_ctzll(hit_b);
+  const int kb = 63 - j;
+  rank -= __shfl(incl_b - cnt, j, 64);
+  base = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    RequestSplits r{0, -1, 0, 0, -1, -1};
+    if (c + lane < p.B) r = request_splits(p, c + lane);
+    const int m = (r.pf == kb) + (r.pl == kb);
+    const int incl = wave_incl_scan(m);
+    const int tot = __shfl(incl, 63, 64);
+    if (rank < base + tot) {
+      const int rel = rank - base;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(rel >= incl - m && rel < incl);
+      const int src = (int)__builtin_ctzll(hit);
+      const int sv = (rel == incl - m && r.pf == kb) ? r.s0 : r.s1;
+      b_out = c + src;
+      s_out = __shfl(sv, src, 64);
+      return true;
+    }
+    base += tot;
+  }
+  return false;
+}
 }  // namespace
 
 // GR = padded number of query heads handled per workgroup (1, 2, 4 or 8).
@@ -409,13 +526,20 @@ void decode_split_heads_kernel(DecodeParams p) {
   auto o_part = [&](int w_) { return reinterpret_cast<float*>(&k_lds[w_][0]); };   // [16][D]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // grid = (head set x query subgroup, split, request), or 1-D over (plan
+  // grid = (head set x query subgroup, split, request), or 1-D over (work
   // item, head set x query subgroup) with the workgroups of one item
-  // adjacent.  More than GM query heads per KV head (NH = 2 only): subgroup
-  // sub takes queries GM*sub..GM*sub+GM-1 of each KV head of the set.
+  // adjacent, the item taken from the plan or found by self_order_item.  More
+  // than GM query heads per KV head (NH = 2 only): subgroup sub takes queries
+  // GM*sub..GM*sub+GM-1 of each KV head of the set.
   const int per = (p.Hkv / NH) * p.sub_groups;
   int s, b, hsub;
-  if (p.planned) {
+  if (p.self_order) {
+    const int item = blockIdx.x / per;
+    hsub = blockIdx.x - item * per;
+    if (!self_order_item(p, item, reinterpret_cast<int*>(&p_lds[wave][0][0]), b, s)) return;
+    b = __builtin_amdgcn_readfirstlane(b);
+    s = __builtin_amdgcn_readfirstlane(s);
+  } else if (p.planned) {
     const int item = blockIdx.x / per;
     hsub = blockIdx.x - item * per;
     const __attribute__((address_space(4))) int* pc =
@@ -726,15 +850,11 @@ static void launch_split(const DecodeParams& p, int rows, hipStream_t stream) {
   }
 }
 
-// The unplanned call's work order, made on the device in one workgroup: every
-// (request, split) that holds a visible key, the full splits first (request
-// by request), then the partial ones (a request's first split under a window
-// and its last) by size, largest first (64 size buckets), then -1 for the
-// remaining slots of the B x max_splits list, which the split kernel skips.
-// Small splits go last, so the launch's tail is short; the result does not
-// depend on the order (within a bucket it is whatever the LDS counters give).
+// The unplanned call's work order (see above), written by one workgroup for
+// the kernels that do not find their own items, then -1 for the remaining
+// slots of the B x max_splits list, which the split kernel skips; within a
+// bucket the order is whatever the LDS counters give.
 constexpr int kOrderThreads = 1024;
-constexpr int kOrderBuckets = 64;
 
 __global__ __launch_bounds__(kOrderThreads)
 void decode_order_kernel(DecodeParams p) {
@@ -751,7 +871,7 @@ void decode_order_kernel(DecodeParams p) {
     s1 = len > 0 ? (len - 1) / S : s0 - 1;
   };
   auto keys_in = [&](int s, int lo, int len) { return min(len, s * S + S) - max(s * S, lo); };
-  auto bucket = [&](int keys) { return (int)(((int64_t)keys * kOrderBuckets - 1) / S); };   // 0..63
+  auto bucket = [&](int keys) { return size_bucket(keys, S); };   // 0..63
   // exclusive scan of one value per thread over the workgroup (Hillis-Steele)
   auto scan = [&](int* a, int v) {
     a[tid] = v;
@@ -831,10 +951,16 @@ template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p_in, int rows, hipStream_t stream) {
   DecodeParams p = p_in;
   // Without a host plan the split grid takes the device-made order when the
-  // 1-D grid over every slot fits; else one workgroup per (request, split) slot.
+  // 1-D grid over every slot fits: found by each workgroup of the head-set
+  // kernel for small batches, else written by the order kernel; otherwise one
+  // workgroup per (request, split) slot.
   const int nh = head_set(p);
   const int64_t per = nh > 0 ? (int64_t)p.Hkv / nh * p.sub_groups : (int64_t)p.Hkv * p.sub_groups;
-  if (!p.planned && (int64_t)p.B * p.max_splits * per * kDecodeThreads < ((int64_t)1 << 32)) {
+  const bool fits = (int64_t)p.B * p.max_splits * per * kDecodeThreads < ((int64_t)1 << 32);
+  if (!p.planned && fits && nh > 0 && p.B <= kSelfOrderMaxB) {
+    p.self_order = true;
+    p.num_items = p.B * p.max_splits;
+  } else if (!p.planned && fits) {
     hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -845,7 +971,8 @@ static hipError_t launch_decode_d(const DecodeParams& p_in, int rows, hipStream_
   // an empty plan (every request has length 0): the merge alone writes O = 0
   if (!p.planned || p.num_items > 0) {
     if (nh > 0) {
-      const dim3 grid = p.planned ? dim3((unsigned)(p.num_items * per)) : dim3((unsigned)per, p.max_splits, p.B);
+      const dim3 grid = p.planned || p.self_order ? dim3((unsigned)(p.num_items * per))
+                                                  : dim3((unsigned)per, p.max_splits, p.B);
       const bool nt = p.sub_groups == 1;
       if (nh == 4) hipLaunchKernelGGL((decode_split_heads_kernel<D, 4, true>), grid, dim3(kDecodeThreads), 0, stream, p);
       else if (nt) hipLaunchKernelGGL((decode_split_heads_kernel<D, 2, true>), grid, dim3(kDecodeThreads), 0, stream, p);

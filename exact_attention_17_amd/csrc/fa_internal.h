@@ -123,6 +123,7 @@ struct DecodeParams {
   const int* plan;         // planned: (request, split) pairs, one per item
   int num_items;
   int* order;              // workspace: the unplanned call's item list, made on the device
+  bool self_order;         // unplanned, head-set kernel: each workgroup finds its own item
   // score modifiers, as in PrefillParams (cap_in = 0 and alibi = NULL: off)
   float cap_in, cap_out;
   const float* alibi;

@@ -588,6 +588,27 @@ def test_decode_many_requests(fa, Hq, Hkv, d):
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,wl", [(200, 32, 8, 700), (256, 64, 8, -1), (65, 16, 4, 300)])
+def test_decode_self_ordered_batches(fa, B, Hq, Hkv, wl):
+    """Unplanned head-set launches of up to 256 requests find their own work
+    items (several 64-request passes): lengths from 0 to 3000 with 256-token
+    splits, with and without a window, so full, partial-first, partial-last and
+    empty requests mix; the result agrees with the oracle, and bit for bit
+    with the planned run over the same cache."""
+    rng = np.random.default_rng(4000 + B + Hq)
+    lens = [int(x) for x in rng.integers(0, 3001, B)]
+    lens[0], lens[-1] = 0, 512
+    ps, split = 16, 256
+    npages = sum(-(-l // ps) for l in lens) + 3
+    w = workloads.random_paged(4100 + B, lens, Hq, Hkv, 128, ps, npages, split,
+                               max_blocks=190, window_left=wl)
+    o, lse = run_decode(fa, w)
+    O, LSE = decode_ref(w)
+    check(f"decode self-ordered B{B} h{Hq} kv{Hkv} w{wl}", o, lse, O, LSE)
+    o2, lse2 = run_decode_planned(fa, w)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+
+
 # ------------------------------------------------ wide-tile kernel (d = 128)
 # fa_fwd takes the 256-row wide-tile kernel for head_dim 128 from 4096 query
 # rows on; these cases sit just past that, with ragged 256-row and 64-key
