@@ -16,8 +16,8 @@ Before the W warmup steps each workload runs untimed for --prewarm-ms of wall
 time: the GPU raises its engine clock only after some milliseconds of
 sustained load.
 
-"roofline" covers the dominant kernel of the step (the prefill kernel on the
-main workload): achieved = algorithmic FLOPs per launch / mean launch
+"roofline" covers the dominant kernel of the step (the wide-tile prefill
+kernel, which fa_fwd takes for head_dim 128 from 4096 query rows on): achieved = algorithmic FLOPs per launch / mean launch
 duration from those events, against the bf16 dense MFMA peak.  "traffic" is
 HBM bytes per launch from the committed rocprofv3 counter summary for that
 kernel and workload, null if the kernel source changed since it was taken.
@@ -49,10 +49,12 @@ PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E (published)
 METRIC = "prefill attn TFLOP/s (% MFMA peak); paged-decode KV GB/s (% HBM peak)"
 PREFILL_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "prefill_fwd.hip")
+WIDE_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "prefill_wide.hip")
 DECODE_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "decode_paged.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 << 20             # plain device copy used to calibrate the byte counters
-PREFILL_KERNEL = "prefill_fwd_kernel<128, 0, false>"
+PREFILL_KERNEL = "prefill_fwd_kernel<128, 0, false>"   # head_dim 128, fewer than 4096 query rows
+WIDE_KERNEL = "prefill_fwd_wide_kernel"                 # head_dim 128, from 4096 query rows on
 
 
 def visible_pairs(Lq, Lk, causal, wl, wr):
@@ -281,8 +283,8 @@ def bench_main(fa, w3, flops3, args):
         "config": {"workload": w3.name, "B": B, "Hq": Hq, "Hkv": w3.k.shape[2], "L": L, "d": d,
                    "causal": True, "flops_per_step": flops3},
         "roofline": roofline_block("mfma", flops3, dur, "TFLOP/s", PEAK_BF16_TFLOPS, 1e9,
-                                   load_traffic("prefill_fwd_causal_gqa_long_traffic", PREFILL_SRC),
-                                   PREFILL_KERNEL),
+                                   load_traffic("prefill_fwd_wide_causal_gqa_long_traffic", WIDE_SRC),
+                                   WIDE_KERNEL),
     }
 
 

@@ -29,8 +29,12 @@
 //   * One wave per SIMD means no other wave hides this wave's VALU work, so
 //     each step is one hand-ordered sequence: 64 MFMA slots (S^T of tile j+1
 //     and P V of tile j-1, alternating), the softmax of tile j spread over
-//     them two slots per score pair, and each LDS fragment read issued two
-//     fragments ahead of its MFMAs.  Scheduling barriers keep that order.
+//     them one score element per slot in three pipelined stages (scale,
+//     exponential, row sum and pack), so that no VALU instruction waits on
+//     one of its own slot, and each LDS fragment read issued one fragment
+//     ahead of its MFMAs.  Scheduling barriers keep that order.  The VALU,
+//     LDS and load instructions of a step then take about as many issue
+//     cycles as its 64 MFMAs run, which is what bounds this kernel.
 //   * Base-2 softmax with the lazy 2^8 rescale of the narrow kernel; the rare
 //     rescale reads and writes the AGPR accumulators in a cold branch.
 #include "fa_internal.h"
@@ -306,7 +310,8 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
     }
   };
   // score pair i (0..31) of the tile: block (qb, kh) = i / 8 in the order
-  // (0,0) (1,0) (0,1) (1,1), elements 2 r2 and 2 r2 + 1 with r2 = i % 8
+  // (0,0) (1,0) (0,1) (1,1), elements 2 r2 and 2 r2 + 1 with r2 = i % 8 (the
+  // redo path; the block uses the pipelined stages below)
   float mb[QB];
   auto sm_pair = [&](const f32x16 (&Sc)[QB][2], u32x4 (&Pc)[QB][4], auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
@@ -317,6 +322,34 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
     l_a[qb] += p0;
     l_b[qb] += p1;
     Pc[qb][2 * kh + (r2 >> 2)][r2 & 3] = pack_bf16x2(p0, p1);
+  };
+
+  // Softmax of one score element per MFMA slot, software-pipelined: element e
+  // (0..63) is score 2 r2 + (e & 1) of pair i = e / 2 (block (qb, kh) = i / 8 in
+  // the order (0,0) (1,0) (0,1) (1,1), r2 = i % 8).  Slot s finishes element s
+  // (row-sum add; the pack of the pair on odd e), takes the exponential of
+  // element s + 1 and scales element s + 2, so no instruction of a slot waits
+  // for another of the same slot.
+  auto el_a = [&](const f32x16 (&Sc)[QB][2], float (&xs)[64], auto ec) __attribute__((always_inline)) {
+    constexpr int e = decltype(ec)::value;
+    if constexpr (e < 64) {
+      constexpr int i = e >> 1, blk = i >> 3, r2 = i & 7, qb = blk & 1, kh = blk >> 1;
+      xs[e] = fmaf(Sc[qb][kh][2 * r2 + (e & 1)], c, -mb[qb]);
+    }
+  };
+  auto el_b = [&](const float (&xs)[64], float (&ps)[64], auto ec) __attribute__((always_inline)) {
+    constexpr int e = decltype(ec)::value;
+    if constexpr (e < 64) ps[e] = exp2_fast(xs[e]);
+  };
+  auto el_c = [&](const float (&ps)[64], u32x4 (&Pc)[QB][4], auto ec) __attribute__((always_inline)) {
+    constexpr int e = decltype(ec)::value;
+    constexpr int i = e >> 1, blk = i >> 3, r2 = i & 7, qb = blk & 1, kh = blk >> 1;
+    if constexpr ((e & 1) == 0) {
+      l_a[qb] += ps[e];
+    } else {
+      l_b[qb] += ps[e];
+      Pc[qb][2 * kh + (r2 >> 2)][r2 & 3] = pack_bf16x2(ps[e - 1], ps[e]);
+    }
   };
 
   // ---- prologue: Q fragments (global -> AGPR), K(0), K(1) -> LDS; S^T(0) -----
@@ -397,6 +430,10 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
     u32x4 kf[2], vf[2];
     kf[0] = k_frag(nxt, 0);
     if constexpr (!FIRST) vf[0] = v_frag(nxt, 0);
+    float xs[64], ps[64];
+    el_a(Sc, xs, std::integral_constant<int, 0>{});
+    el_a(Sc, xs, std::integral_constant<int, 1>{});
+    el_b(xs, ps, std::integral_constant<int, 0>{});
     sched_fence();
     static_for<0, 64>([&](auto slot) __attribute__((always_inline)) {
       constexpr int s = decltype(slot)::value;
@@ -405,10 +442,12 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
       if constexpr ((s & 1) == 0) {
         if constexpr ((g & 7) == 0) mma_s_first(Sn[qb][g >> 3], kf[g & 1], qf[qb][g & 7]);
         else mma_s(Sn[qb][g >> 3], kf[g & 1], qf[qb][g & 7]);
-        sm_pair(Sc, Pc, std::integral_constant<int, (s >> 1)>{});
       } else if constexpr (!FIRST) {
         mma_o(oacc[qb][g & 3], vf[g & 1], Pp[qb][g >> 2]);
       }
+      el_c(ps, Pc, std::integral_constant<int, s>{});
+      el_b(xs, ps, std::integral_constant<int, s + 1>{});
+      el_a(Sc, xs, std::integral_constant<int, s + 2>{});
       // one fragment ahead: fragment g + 1 goes into the buffer fragment g - 1
       // left, whose last MFMA was in the previous slot group
       if constexpr ((s & 3) == 0 && g + 1 < 16) {
