@@ -427,7 +427,7 @@ def bench_decode(fa, args, extras):
     od = torch.empty_like(qd)
     ld = torch.empty((64, 32), dtype=torch.float32, device="cuda")
     nb = decode_bytes(w4)
-    kernels = "decode_order + decode_split_heads<128,4,nt> + decode_merge"
+    kernels = "decode_split_heads<128,4,nt> (self-ordered) + decode_merge"
     _, dur = timed_steps(lambda: fa.fa_decode_paged(qd, kc, vc, bt, sl, w4.scale, -1, 512, out=od,
                                                     lse=ld, workspace=ws),
                          args.steps, args.warmup, args.prewarm_ms)
