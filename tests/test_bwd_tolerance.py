@@ -1,7 +1,8 @@
 """The backward tolerance (tests/bwd_tolerance.py) is not vacuous: the float64
 oracle rounded once to bf16 passes it, and plausible kernel mistakes -- a key
 tile dropped from dQ, a missing delta term, the wrong scale on dK, one row's
-contribution lost from dV -- each exceed it (checked on the CPU)."""
+contribution lost from dV -- each exceed it (checked on the CPU).  Smaller
+ones too: one key missing from dQ, dQ 3% or dK 4% too large."""
 
 import numpy as np
 
@@ -53,3 +54,17 @@ def test_tolerance_passes_rounded_oracle_and_catches_mistakes():
     _, _, P = oracle.attend_rows(Q, K, V, scale, vis)
     dq_nodelta = scale * (P * (DO @ V.T)) @ K
     assert ratio(dq_nodelta, ref[0][0, :, 0], tol[0][0, :, 0]) > 1
+
+
+def test_tolerance_catches_small_mistakes():
+    """One key's contribution missing from dQ (the last key, seen by the last
+    rows only) and a few percent of scale error on dQ or dK."""
+    q, k, v, do, scale, causal, window = case()
+    ref = oracle.attention_bwd_ref(q, k, v, do, scale, causal, window)
+    tol = bwd_tolerance(q, k, v, do, scale, causal, window, ref)
+    k_one = np.array(k)
+    k_one[:, 150] = 0
+    dq_one = oracle.attention_bwd_ref(q, k_one, v, do, scale, causal, window)[0]
+    assert ratio(dq_one, ref[0], tol[0]) > 2
+    assert ratio(ref[0] * 1.03, ref[0], tol[0]) > 1
+    assert ratio(ref[1] * 1.04, ref[1], tol[1]) > 1
