@@ -67,6 +67,14 @@ FA_DEV void mma_o(f32x16& d, const u32x4& a, const u32x4& b) { d = mfma32x32x16(
 // before a VALU instruction reads it (or writes one of its operands): 26 cycles
 // of the issuing wave, more than the 8-pass MFMA's requirement.
 FA_DEV void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1" ::: "memory"); }
+// lds_load16 with one wait state (for the M0 write just before) instead of
+// five: the kernel's load offsets and descriptors come from scalar
+// arithmetic, not from VALU writes of SGPRs (checked in the compiled code by
+// isa_check.check_lds_loads).
+FA_DEV void lds_load16_m0(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(lds_base) : "memory");
+}
 // No instruction may be scheduled across this point.
 FA_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 // Pins a value in AGPRs at this point: copies into it (v_accvgpr_write) must
@@ -180,7 +188,7 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const uint32_t soff = (uint32_t)(kb + 4 * i * RPI) * k_row_bytes;
-      lds_load16(rs, src, (uint32_t)__builtin_amdgcn_readfirstlane(soff), dst + wave_lds + 4096u * i);
+      lds_load16_m0(rs, src, (uint32_t)__builtin_amdgcn_readfirstlane(soff), dst + wave_lds + 4096u * i);
     }
   };
 

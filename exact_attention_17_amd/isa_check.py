@@ -95,6 +95,46 @@ def check_asm(text, before=3, after=19):
     return found
 
 
+_SGPR_RANGE = re.compile(r"s\[(\d+):(\d+)\]$")
+_SGPR = re.compile(r"s(\d+)$")
+
+
+def _sregs(tok):
+    """SGPR names covered by one operand token (s7, s[4:7], m0)."""
+    m = _SGPR_RANGE.match(tok)
+    if m:
+        return {f"s{i}" for i in range(int(m.group(1)), int(m.group(2)) + 1)}
+    if _SGPR.match(tok) or tok == "m0":
+        return {tok}
+    return set()
+
+
+def check_lds_loads(text, valu_sgpr=5, m0=1):
+    """Hazards of inline-assembly direct-to-LDS buffer loads in `text`: a VALU
+    instruction (v_readfirstlane and the like) writing one of the load's SGPR
+    operands within `valu_sgpr` wait states before it, or an M0 write within
+    `m0` wait states before it.  An empty list means none."""
+    insts = _instructions(text)
+    found = []
+    for i, (op, args, asm) in enumerate(insts):
+        if not (asm and op.startswith("buffer_load") and "lds" in args):
+            continue
+        sg = set().union(*(_sregs(a) for a in args[1:4]))
+        k, ws = i - 1, 0
+        while k >= 0 and ws < max(valu_sgpr, m0):
+            op2, args2, _ = insts[k]
+            if op2.startswith(("s_branch", "s_cbranch")) or op2.endswith(":"):
+                break
+            dst = _sregs(args2[0]) if args2 else set()
+            if op2.startswith("v_") and ws < valu_sgpr and dst & sg:
+                found.append(f"{op2} {args2[0]} written {ws} wait states before {op} {' '.join(args)}")
+            if "m0" in dst and ws < m0:
+                found.append(f"{op2} m0 written {ws} wait states before {op} {' '.join(args)}")
+            ws += _wait_states(op2, args2)
+            k -= 1
+    return found
+
+
 def compile_to_asm(source="prefill_wide.hip"):
     """gfx950 assembly of one source file, compiled as the library is."""
     with tempfile.TemporaryDirectory() as tmp:
@@ -110,6 +150,7 @@ def compile_to_asm(source="prefill_wide.hip"):
 
 
 if __name__ == "__main__":
-    problems = check_asm(compile_to_asm(*(sys.argv[1:2] or [])))
+    text = compile_to_asm(*(sys.argv[1:2] or []))
+    problems = check_asm(text) + check_lds_loads(text)
     print("\n".join(problems) or "no inline-asm MFMA hazards")
     sys.exit(1 if problems else 0)

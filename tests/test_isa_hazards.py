@@ -1,7 +1,9 @@
-"""The wide prefill kernel's inline-assembly MFMAs, checked in the compiled
-gfx950 assembly (no GPU needed): no VALU write of an operand right before one,
-no read of a result right after one (the hardware wait states the compiler
-does not insert for instructions it cannot see)."""
+"""The wide prefill kernel's inline-assembly MFMAs and direct-to-LDS loads,
+checked in the compiled gfx950 assembly (no GPU needed): no VALU write of an
+MFMA operand right before one, no read of an MFMA result right after one, no
+VALU write of a load's SGPR operands within 5 wait states and no M0 write
+right before a load (the hardware wait states the compiler does not insert
+for instructions it cannot see)."""
 
 import pytest
 
@@ -17,6 +19,33 @@ def test_wide_kernel_has_no_inline_mfma_hazards(wide_asm):
     assert "v_mfma_f32_32x32x16_bf16" in wide_asm
     problems = isa_check.check_asm(wide_asm)
     assert problems == [], "\n".join(problems[:20])
+
+
+def test_wide_kernel_lds_loads_have_their_wait_states(wide_asm):
+    assert "offen lds" in wide_asm
+    problems = isa_check.check_lds_loads(wide_asm)
+    assert problems == [], "\n".join(problems[:20])
+
+
+def test_lds_load_checker_flags_planted_hazards():
+    bad = """
+    v_readfirstlane_b32 s12, v3
+    s_mov_b32 m0, s40
+    ;;#ASMSTART
+    buffer_load_dwordx4 v2, s[24:27], s12 offen lds
+    ;;#ASMEND
+    """
+    assert len(isa_check.check_lds_loads(bad)) == 2
+    good = """
+    v_readfirstlane_b32 s12, v3
+    s_nop 3
+    s_mov_b32 m0, s40
+    ;;#ASMSTART
+    s_nop 0
+    buffer_load_dwordx4 v2, s[24:27], s12 offen lds
+    ;;#ASMEND
+    """
+    assert isa_check.check_lds_loads(good) == []
 
 
 def test_checker_flags_planted_hazards():
