@@ -120,13 +120,18 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   // outweighs that below a few thousand query rows.  Everything else takes the
   // narrow kernel (128 rows; two workgroups per CU at head_dim 128, three at 64).
   const bool wide = d == 128 && Lq >= fa::kWideMinRows;
-  const int rows = wide ? fa::kWideRows : fa::kBlockM;
+  // A wide workgroup takes 4 query heads of one KV group when the group size
+  // allows (64 rows each: its waves share every K/V tile and meet the causal
+  // diagonal in one step instead of four), else 2 heads of 128 rows or one of 256.
+  p.wide_heads = !wide ? 1 : p.group % 4 == 0 ? 4 : p.group % 2 == 0 ? 2 : 1;
+  const int rows = wide ? fa::kWideRows / p.wide_heads : fa::kBlockM;
   const int slots = wide ? fa::kWideSlotsPerXcd : fa::kPrefillSlotsPerXcd;
   p.num_q_tiles = (int)cdiv(Lq, rows);
   p.xcd_groups = xcd_groups(B * Hkv);
   // KV groups per XCD chunk: about one XCD's worth of resident workgroups
-  p.chunk_groups = (int)std::max<int64_t>(1, slots / ((int64_t)p.group * p.num_q_tiles));
-  if ((int64_t)p.num_q_tiles * B * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
+  p.chunk_groups = (int)std::max<int64_t>(
+      1, slots / ((int64_t)(p.group / p.wide_heads) * p.num_q_tiles));
+  if ((int64_t)p.num_q_tiles * B * (Hq / p.wide_heads) >= kMaxElems) return FA_ERR_INVALID_ARG;
   hipError_t e = wide ? fa::launch_prefill_wide(p, static_cast<hipStream_t>(stream))
                       : fa::launch_prefill(p, d, 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

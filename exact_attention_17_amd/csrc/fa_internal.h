@@ -19,8 +19,9 @@ constexpr int kDecodeChunk = 64;     // keys per wave iteration
 constexpr int kDefaultSplit = 512;
 // Prefill workgroups resident per XCD (32 CUs x 2), used to size work chunks.
 constexpr int kPrefillSlotsPerXcd = 64;
-// Wide-tile prefill (head_dim 128, dense): 256 query rows per workgroup, one
-// workgroup per CU.
+// Wide-tile prefill (head_dim 128, dense): 256 (query row, head) pairs per
+// workgroup -- 64 rows of 4 heads of one KV group, 128 rows of 2, or 256 rows
+// of one -- one workgroup per CU.
 constexpr int kWideRows = 256;
 constexpr int kWideSlotsPerXcd = 32;
 constexpr int kWideMinRows = 4096;   // query rows from which fa_fwd takes it
@@ -46,6 +47,7 @@ struct PrefillParams {
   int num_q_tiles;         // dense: ceil(Lq / kBlockM); varlen: tile slots or plan items
   int xcd_groups;          // >0: XCD-aware work mapping with this many KV groups
   int chunk_groups;        // KV groups an XCD works on together (dense mapping)
+  int wide_heads;          // wide kernel: query heads of one KV group per workgroup (1, 2, 4)
   // paged KV cache (chunked prefill): k/v are the page pools
   // [num_pages][page_size][Hkv][d]; request b has cache_seqlens[b] + append_len keys
   const int* block_table;  // [B][max_blocks]
@@ -133,7 +135,8 @@ struct DecodeParams {
 
 // mode: 0 dense, 1 varlen, 2 paged KV cache
 hipError_t launch_prefill(const PrefillParams& p, int d, int mode, hipStream_t stream);
-// dense, head_dim 128; p.num_q_tiles and p.chunk_groups sized for kWideRows
+// dense, head_dim 128; p.num_q_tiles and p.chunk_groups sized for
+// kWideRows / p.wide_heads rows of p.wide_heads query heads per workgroup
 hipError_t launch_prefill_wide(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, int rows, hipStream_t stream);

@@ -8,12 +8,16 @@
 // sec. 3.2-3.3 and its GQA appendix); only the mapping onto the chip differs.
 //
 // Mapping onto CDNA4:
-//   * One workgroup = 4 wave64s = 256 query rows of one (batch, head); each
-//     wave owns 64 rows as two 32-row blocks, and one workgroup fills a CU
-//     (one wave per SIMD, 512 registers per lane).  Every K or V operand
-//     fragment read from LDS then feeds two MFMAs, one per row block, which
-//     halves LDS read bytes per MFMA against 32 rows per wave; the per-CU K/V
-//     tile loads (direct-to-LDS) halve too, since a tile serves 256 rows.
+//   * One workgroup = 4 wave64s = 256 (query row, head) pairs of one batch
+//     and KV group: 64 rows of each of 4 query heads when the GQA group size
+//     is a multiple of 4 (all waves then reach the causal diagonal in the
+//     same step), 128 rows of 2 heads when it is even, else 256 rows of one
+//     head.  Each wave owns 64 rows of one head as two 32-row blocks, and one
+//     workgroup fills a CU (one wave per SIMD, 512 registers per lane).  Every
+//     K or V operand fragment read from LDS then feeds two MFMAs, one per row
+//     block, which halves LDS read bytes per MFMA against 32 rows per wave;
+//     the per-CU K/V tile loads (direct-to-LDS) halve too, since a tile
+//     serves 256 query rows.
 //   * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16):
 //     K rows are the A operand from LDS, Q rows the B operand, so each lane
 //     holds one query row of a 32x32 tile and the row sum needs no cross-lane
@@ -31,10 +35,11 @@
 //     and P V of tile j-1, alternating), the softmax of tile j spread over
 //     them one score element per slot in three pipelined stages (scale,
 //     exponential, row sum and pack), so that no VALU instruction waits on
-//     one of its own slot, and each LDS fragment read issued one fragment
-//     ahead of its MFMAs.  Scheduling barriers keep that order.  The VALU,
-//     LDS and load instructions of a step then take about as many issue
-//     cycles as its 64 MFMAs run, which is what bounds this kernel.
+//     one of its own slot, each LDS fragment read issued one fragment ahead
+//     of its MFMAs, and the step's eight direct-to-LDS tile loads one every
+//     four slots of the first half.  Scheduling barriers keep that order.
+//     The VALU, LDS and load instructions of a step then take about as many
+//     issue cycles as its 64 MFMAs run, which is what bounds this kernel.
 //   * Base-2 softmax with the lazy 2^8 rescale of the narrow kernel; the rare
 //     rescale reads and writes the AGPR accumulators in a cold branch.
 #include "fa_internal.h"
@@ -127,12 +132,21 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
   const int n = lane & 31, hi = lane >> 5;
   const int i16 = lane & 15, g16 = lane >> 4;
 
-  WorkItem w = map_work_dense(p, blockIdx.x);
+  // The workgroup owns GW query heads of one KV group (a "head set") and RW
+  // rows of each; wave w takes head w % GW and the 64-row block w / GW.  The
+  // dense work order runs over head sets as if they were heads.
+  const int GW = p.wide_heads;
+  const int RW = kWideRows / GW;
+  struct HeadSetView { int B, Hq, Hkv, group, num_q_tiles, xcd_groups, chunk_groups, Lq, Lk; };
+  const HeadSetView hs = {p.B, p.Hq / GW, p.Hkv, p.group / GW, p.num_q_tiles, p.xcd_groups,
+                          p.chunk_groups, p.Lq, p.Lk};
+  WorkItem w = map_work_dense(hs, blockIdx.x);
   // the work item is the same in every lane: keep it in scalar registers so
   // every buffer descriptor built from it is an SGPR operand
   w.b = __builtin_amdgcn_readfirstlane(w.b);
-  w.h = __builtin_amdgcn_readfirstlane(w.h);
+  w.h = __builtin_amdgcn_readfirstlane(w.h * GW + wave % GW);   // this wave's head
   w.qt = __builtin_amdgcn_readfirstlane(w.qt);
+  const int rblk = wave / GW;
   const int Lq = __builtin_amdgcn_readfirstlane(w.Lq), Lk = __builtin_amdgcn_readfirstlane(w.Lk);
   const int kvh = w.h / p.group;
   const int delta = Lk - Lq;
@@ -143,7 +157,7 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
   float* lseg = p.lse ? p.lse + ((int64_t)w.b * p.Hq + w.h) * p.lse_seq_stride : nullptr;
 
   // ---- key ranges: workgroup, wave, and each of the lane's two rows -------
-  const int q0 = w.qt * kWideRows;
+  const int q0 = w.qt * RW;
   auto key_lo = [&](int row) __attribute__((always_inline)) { return p.win_left >= 0 ? max(0, row + delta - p.win_left) : 0; };
   auto key_hi = [&](int row) __attribute__((always_inline)) {    // exclusive
     int e = Lk;
@@ -152,11 +166,11 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
     return e;
   };
   const int kv_lo = key_lo(q0);
-  const int kv_hi = key_hi(min(q0 + kWideRows, Lq) - 1);
+  const int kv_hi = key_hi(min(q0 + RW, Lq) - 1);
   const int kt_begin = kv_lo / kBlockN;
   const int kt_end = kv_hi > kv_lo ? (kv_hi + kBlockN - 1) / kBlockN : kt_begin;
   const int ntiles = kt_end - kt_begin;
-  const int qw0 = q0 + 64 * wave;
+  const int qw0 = q0 + 64 * rblk;
   const int rw0 = min(qw0, Lq - 1), rw1 = min(qw0 + 63, Lq - 1);
   const int wlo_last = key_lo(rw1), whi_first = key_hi(rw0);
   // the lane's query row in block qb; the masks recompute their bounds from
@@ -406,7 +420,9 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
     }
     // A row that has seen no key yet needs its max up front; a raise then
     // first adds the pending P V (relative to the old max) and clears it.
-    const bool exact = wave_any(m_ref[0] == -INFINITY || m_ref[1] == -INFINITY);
+    // Past the first key of the wave's last row every row with a visible key
+    // has a finite max, so the vote is skipped from there on.
+    const bool exact = kb <= wlo_last && wave_any(m_ref[0] == -INFINITY || m_ref[1] == -INFINITY);
     if (exact) {
       float al[QB];
       bool need[QB];
@@ -428,16 +444,17 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
         mfma_drain();
       }
     }
-    if (j + 2 < ntiles) fetch(krs, k_src, k_lds_addr + cur * TILE_BYTES, kb + 2 * kBlockN);
-    fetch(vrs, v_src, v_lds_addr + cur * TILE_BYTES, kb);
     const float la0[QB] = {l_a[0], l_a[1]}, lb0[QB] = {l_b[0], l_b[1]};
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mb[qb] = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
 
     // the interleaved block
+    // V fragments are read before K ones: the wait for a K fragment before an
+    // S^T MFMA then also covers the V fragment of the P V MFMA after it, so
+    // a slot pair needs one LDS wait instead of two
     u32x4 kf[2], vf[2];
-    kf[0] = k_frag(nxt, 0);
     if constexpr (!FIRST) vf[0] = v_frag(nxt, 0);
+    kf[0] = k_frag(nxt, 0);
     float xs[64], ps[64];
     el_a(Sc, xs, std::integral_constant<int, 0>{});
     el_a(Sc, xs, std::integral_constant<int, 1>{});
@@ -456,15 +473,33 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
       el_c(ps, Pc, std::integral_constant<int, s>{});
       el_b(xs, ps, std::integral_constant<int, s + 1>{});
       el_a(Sc, xs, std::integral_constant<int, s + 2>{});
+      // The step's tile loads ride in the first half of the block, one 1 KB
+      // load every 4 slots: K(j+2) into the buffer of K(j) and V(j) into that
+      // of V(j-2), both last read in step j-1.  Spread this way their issue
+      // overlaps the MFMAs (a burst of eight before the block took about 300
+      // cycles of the step).  K(j+2) is loaded even past the last tile: rows
+      // beyond the causal range are harmless, rows at or past Lk load zeros,
+      // and such a buffer is only read by the discarded S^T of the last step.
+      if constexpr ((s & 3) == 2 && s < 32) {
+        constexpr int i = s >> 2;
+        if constexpr (i < LOADS) {
+          const uint32_t soff = (uint32_t)(kb + 2 * kBlockN + 4 * i * RPI) * k_row_bytes;
+          lds_load16_m0(krs, k_src, (uint32_t)__builtin_amdgcn_readfirstlane(soff),
+                        k_lds_addr + cur * TILE_BYTES + wave_lds + 4096u * i);
+        } else {
+          const uint32_t soff = (uint32_t)(kb + 4 * (i - LOADS) * RPI) * k_row_bytes;
+          lds_load16_m0(vrs, v_src, (uint32_t)__builtin_amdgcn_readfirstlane(soff),
+                        v_lds_addr + cur * TILE_BYTES + wave_lds + 4096u * (i - LOADS));
+        }
+      }
       // one fragment ahead: fragment g + 1 goes into the buffer fragment g - 1
       // left, whose last MFMA was in the previous slot group
       if constexpr ((s & 3) == 0 && g + 1 < 16) {
-        kf[(g + 1) & 1] = k_frag(nxt, g + 1);
         if constexpr (!FIRST) vf[(g + 1) & 1] = v_frag(nxt, g + 1);
+        kf[(g + 1) & 1] = k_frag(nxt, g + 1);
       }
       sched_fence();
     });
-    mfma_drain();
     // This lane's share of the tile's row sum bounds each of its
     // probabilities (inf and NaN included): above 2^8, take the tile back,
     // raise the max, rescale (P_{j-1} V_{j-1} is already in O) and redo P_j.
@@ -472,6 +507,7 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) redo |= !((l_a[qb] - la0[qb]) + (l_b[qb] - lb0[qb]) <= 256.f);
     if (!exact && wave_any(redo)) {
+      mfma_drain();
       pin_o();
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -485,6 +521,9 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
       mfma_drain();
       static_for<0, 32>([&](auto i) __attribute__((always_inline)) { sm_pair(Sc, Pc, i); });
     }
+    // the next step's VALU reads S^T(j+1); the row-sum check above already
+    // counts toward these wait states
+    mfma_drain();
     lds_load_wait();
     __syncthreads();
   };
@@ -541,7 +580,7 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
 }
 
 hipError_t launch_prefill_wide(const PrefillParams& p, hipStream_t stream) {
-  const int64_t nblocks = (int64_t)p.num_q_tiles * p.B * p.Hq;
+  const int64_t nblocks = (int64_t)p.num_q_tiles * p.B * (p.Hq / p.wide_heads);
   if (nblocks <= 0) return hipSuccess;
   const bool mods = p.cap_in > 0.f || p.alibi != nullptr;
   if (mods)
