@@ -80,6 +80,18 @@ FA_DEV void lds_load16_m0(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t s
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(lds_base) : "memory");
 }
+// M0 <- lds_base for a later lds_load16_after_m0 (the value stays live in M0).
+FA_DEV uint32_t set_m0(uint32_t lds_base) {
+  uint32_t m;
+  asm volatile("s_mov_b32 m0, %1" : "={m0}"(m) : "s"(lds_base));
+  return m;
+}
+// Direct-to-LDS load whose M0 was written by set_m0 at least one instruction
+// earlier, so it needs no wait state of its own.
+FA_DEV void lds_load16_after_m0(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset, uint32_t m) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(m) : "memory");
+}
 // No instruction may be scheduled across this point.
 FA_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 // Pins a value in AGPRs at this point: copies into it (v_accvgpr_write) must
@@ -464,6 +476,12 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
       constexpr int s = decltype(slot)::value;
       constexpr int g = s >> 2;   // fragment index of this slot's MFMA
       constexpr int qb = (s >> 1) & 1;
+      uint32_t m0v = 0;
+      if constexpr ((s & 3) == 2 && s < 32) {
+        constexpr int i = s >> 2;
+        m0v = set_m0(i < LOADS ? k_lds_addr + cur * TILE_BYTES + wave_lds + 4096u * i
+                               : v_lds_addr + cur * TILE_BYTES + wave_lds + 4096u * (i - LOADS));
+      }
       if constexpr ((s & 1) == 0) {
         if constexpr ((g & 7) == 0) mma_s_first(Sn[qb][g >> 3], kf[g & 1], qf[qb][g & 7]);
         else mma_s(Sn[qb][g >> 3], kf[g & 1], qf[qb][g & 7]);
@@ -484,12 +502,10 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
         constexpr int i = s >> 2;
         if constexpr (i < LOADS) {
           const uint32_t soff = (uint32_t)(kb + 2 * kBlockN + 4 * i * RPI) * k_row_bytes;
-          lds_load16_m0(krs, k_src, (uint32_t)__builtin_amdgcn_readfirstlane(soff),
-                        k_lds_addr + cur * TILE_BYTES + wave_lds + 4096u * i);
+          lds_load16_after_m0(krs, k_src, (uint32_t)__builtin_amdgcn_readfirstlane(soff), m0v);
         } else {
           const uint32_t soff = (uint32_t)(kb + 4 * (i - LOADS) * RPI) * k_row_bytes;
-          lds_load16_m0(vrs, v_src, (uint32_t)__builtin_amdgcn_readfirstlane(soff),
-                        v_lds_addr + cur * TILE_BYTES + wave_lds + 4096u * (i - LOADS));
+          lds_load16_after_m0(vrs, v_src, (uint32_t)__builtin_amdgcn_readfirstlane(soff), m0v);
         }
       }
       // one fragment ahead: fragment g + 1 goes into the buffer fragment g - 1
