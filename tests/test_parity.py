@@ -611,9 +611,10 @@ def test_decode_self_ordered_batches(fa, B, Hq, Hkv, wl):
 
 # ------------------------------------------------ wide-tile kernel (d = 128)
 # fa_fwd takes the 256-row wide-tile kernel for head_dim 128 from 4096 query
-# rows on; these cases sit just past that, with ragged 256-row and 64-key
-# tails, so every mask mode, GQA, Lq != Lk, the rescale paths and the score
-# modifiers run through it (the smaller dense cases above take the narrow one).
+# rows on; these cases sit just past that, with ragged row and 64-key tails,
+# so every mask mode, GQA (workgroups of 1, 2 and 4 query heads), Lq != Lk,
+# the rescale paths and the score modifiers run through it (the smaller dense
+# cases above take the narrow one).
 WIDE_CASES = [
     # B, Lq, Lk, Hq, Hkv, causal, window, softcap, alibi
     (1, 4133, 4133, 2, 1, True, (-1, -1), 0.0, "none"),
@@ -624,6 +625,12 @@ WIDE_CASES = [
     (1, 4099, 4099, 2, 1, False, (200, 37), 0.0, "none"),   # two-sided window
     (2, 4097, 4097, 2, 1, True, (-1, -1), 20.0, "head"),    # softcap + ALiBi
     (1, 4160, 4160, 2, 2, True, (64, 0), 0.0, "batch"),
+    # 4 query heads per KV head: 64-row workgroups of 4 heads ("head sets")
+    (1, 4133, 4133, 4, 1, True, (-1, -1), 0.0, "none"),
+    (1, 4500, 4100, 8, 2, True, (-1, -1), 0.0, "none"),     # Lq > Lk, two KV groups
+    (1, 4111, 4111, 8, 1, True, (300, 0), 20.0, "head"),    # two head sets per KV group
+    # 6 query heads per KV head: 2-head workgroups of 128 rows
+    (1, 4100, 4500, 6, 1, False, (200, 37), 0.0, "none"),
 ]
 
 
