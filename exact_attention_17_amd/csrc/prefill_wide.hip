@@ -80,10 +80,13 @@ FA_DEV void lds_load16_m0(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t s
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(lds_base) : "memory");
 }
-// M0 <- lds_base for a later lds_load16_after_m0 (the value stays live in M0).
-FA_DEV uint32_t set_m0(uint32_t lds_base) {
+// M0 <- base + OFF for a later lds_load16_after_m0 (the value stays live in
+// M0).  The sum is formed in M0 itself, so no SGPR holds the eight
+// destinations of a step.
+template <uint32_t OFF>
+FA_DEV uint32_t set_m0(uint32_t base) {
   uint32_t m;
-  asm volatile("s_mov_b32 m0, %1" : "={m0}"(m) : "s"(lds_base));
+  asm volatile("s_add_u32 m0, %1, %2" : "={m0}"(m) : "s"(base), "n"(OFF));
   return m;
 }
 // Direct-to-LDS load whose M0 was written by set_m0 at least one instruction
@@ -479,8 +482,10 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
       uint32_t m0v = 0;
       if constexpr ((s & 3) == 2 && s < 32) {
         constexpr int i = s >> 2;
-        m0v = set_m0(i < LOADS ? k_lds_addr + cur * TILE_BYTES + wave_lds + 4096u * i
-                               : v_lds_addr + cur * TILE_BYTES + wave_lds + 4096u * (i - LOADS));
+        if constexpr (i < LOADS)
+          m0v = set_m0<cur * TILE_BYTES + 4096u * i>(k_lds_addr + wave_lds);
+        else
+          m0v = set_m0<cur * TILE_BYTES + 4096u * (i - LOADS)>(v_lds_addr + wave_lds);
       }
       if constexpr ((s & 1) == 0) {
         if constexpr ((g & 7) == 0) mma_s_first(Sn[qb][g >> 3], kf[g & 1], qf[qb][g & 7]);

@@ -155,3 +155,29 @@ def test_side_stream_calls_match_current_stream_calls(fa):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
         del junk
+
+
+@pytest.mark.parametrize("case", [
+    # B, Lq, Lk, Hq, Hkv, causal, window
+    (1, 4133, 4133, 8, 2, True, (-1, -1)),      # 4-head workgroups of the wide kernel
+    (1, 4500, 4100, 4, 2, True, (-1, -1)),      # 2-head workgroups, Lq > Lk
+    (1, 4100, 4600, 2, 2, True, (700, 0)),      # 1-head workgroups, sliding window
+    (1, 4096, 3000, 6, 1, False, (300, 20)),    # two-sided window, non-causal
+])
+def test_wide_and_narrow_kernels_agree_bitwise(fa, case):
+    """Dense head_dim-128 prefill from 4096 query rows runs the wide-tile kernel
+    (64 rows per wave, up to 4 heads per workgroup); the same problem as a
+    one-sequence varlen batch runs the narrow kernel (32 rows per wave).  Both
+    take the tiles in the same order with the same per-row arithmetic (base-2
+    softmax, the same lazy-rescale decisions per row), so their outputs agree
+    bit for bit: a check of each kernel's tiling against the other's."""
+    B, Lq, Lk, Hq, Hkv, causal, window = case
+    w = workloads.random_dense(60 + Lq + Hq, B, Lq, Lk, Hq, Hkv, 128, causal, window)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    o1, l1 = fa.fa_fwd(q, k, v, w.scale, causal, window)
+    cu_q = torch.tensor([0, Lq], dtype=torch.int32, device="cuda")
+    cu_k = torch.tensor([0, Lk], dtype=torch.int32, device="cuda")
+    o2, l2 = fa.fa_fwd_varlen(q[0], k[0], v[0], cu_q, cu_k, Lq, Lk, w.scale, causal, window)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0].view(torch.int16), o2.view(torch.int16)), case
+    assert torch.equal(l1[0], l2), case
