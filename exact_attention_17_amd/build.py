@@ -18,6 +18,10 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+# The same sources with -DFA_DEBUG: every direct-to-LDS tile load first fills
+# its destination with bf16 NaN, so a missing wait or barrier shows as NaN in
+# the outputs (tests/test_debug_build.py compares it with the release library).
+DEBUG_LIB_PATH = os.path.join(PKG_DIR, "libfa_debug.so")
 SOURCES = ["fa_api.cpp", "plan.cpp", "prefill_fwd.hip", "prefill_wide.hip", "decode_paged.hip",
            "attn_bwd.hip"]
 ARCH = "gfx950"
@@ -40,10 +44,12 @@ def compile_command(out=LIB_PATH, extra=()):
     return cmd
 
 
-def build_library(verbose=False, extra=()):
-    """Compile every HIP source into LIB_PATH (always recompiles)."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = compile_command(tmp, extra)
+def build_library(verbose=False, extra=(), debug=False):
+    """Compile every HIP source into LIB_PATH, or with debug=True into
+    DEBUG_LIB_PATH with -DFA_DEBUG (always recompiles)."""
+    target = DEBUG_LIB_PATH if debug else LIB_PATH
+    tmp = target + ".tmp"
+    cmd = compile_command(tmp, list(extra) + (["-DFA_DEBUG"] if debug else []))
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,9 +60,10 @@ def build_library(verbose=False, extra=()):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_library(verbose=True, debug=True))

@@ -104,6 +104,20 @@ FA_DEV uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
+// Debug builds (-DFA_DEBUG): the 16 bytes that a lane's direct-to-LDS load
+// will write are first set to bf16 NaN and the write is awaited, so a read
+// that a missing wait or barrier lets through returns NaN, which the outputs
+// show, instead of the previous tile's finite data.  Release builds: nothing.
+#ifdef FA_DEBUG
+FA_DEV void lds_poison16(uint32_t lds_base) {
+  *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(lds_base + 16u * (threadIdx.x & 63)) =
+      u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+#else
+FA_DEV void lds_poison16(uint32_t) {}
+#endif
+
 // 16-byte buffer load that writes LDS instead of VGPRs: lane l reads bytes
 // [voffset + soffset, +16) of the buffer and stores them at LDS byte
 // lds_base + 16 l (soffset and lds_base must be wave-uniform; lds_base goes
@@ -114,6 +128,7 @@ FA_DEV uint32_t lds_address(const void* p) {
 // states before a VMEM read, and M0 one before an LDS-destination load, so 5
 // are inserted here.
 FA_DEV void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset, uint32_t lds_base) {
+  lds_poison16(lds_base);
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(lds_base) : "memory");
 }

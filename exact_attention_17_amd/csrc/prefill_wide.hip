@@ -77,6 +77,7 @@ FA_DEV void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 
 // arithmetic, not from VALU writes of SGPRs (checked in the compiled code by
 // isa_check.check_lds_loads).
 FA_DEV void lds_load16_m0(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset, uint32_t lds_base) {
+  lds_poison16(lds_base);
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(lds_base) : "memory");
 }
@@ -92,6 +93,7 @@ FA_DEV uint32_t set_m0(uint32_t base) {
 // Direct-to-LDS load whose M0 was written by set_m0 at least one instruction
 // earlier, so it needs no wait state of its own.
 FA_DEV void lds_load16_after_m0(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset, uint32_t m) {
+  lds_poison16(m);
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(m) : "memory");
 }
