@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 # the outputs (tests/test_debug_build.py compares it with the release library).
 DEBUG_LIB_PATH = os.path.join(PKG_DIR, "libfa_debug.so")
 SOURCES = ["fa_api.cpp", "plan.cpp", "prefill_fwd.hip", "prefill_wide.hip", "decode_paged.hip",
-           "attn_bwd.hip"]
+           "attn_bwd.hip", "debug_checks.hip"]
 ARCH = "gfx950"
 
 

@@ -1,6 +1,7 @@
 // C-ABI entry points: argument validation, planning and kernel dispatch.
 // Every check runs on the host before any HIP call; a failed check returns a
-// status and enqueues nothing.
+// status and enqueues nothing.  Debug builds (-DFA_DEBUG) then check the
+// device-side preconditions with one small kernel before the real work.
 #include "fa.h"
 #include "fa_internal.h"
 
@@ -19,6 +20,38 @@ constexpr int64_t kMaxBatchElems = (int64_t)1 << 30;   // bf16 elements: < 2^31 
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The device-side preconditions (offsets, key counts, page ids), checked on
+// the device in debug builds (-DFA_DEBUG) after every host check and before
+// any other work is enqueued; a violation returns FA_ERR_INVALID_ARG.
+// Release builds check nothing here.
+fa_status device_checks(const fa::DeviceChecks& c, void* stream) {
+#ifdef FA_DEBUG
+  const int r = fa::debug_check_inputs(c, static_cast<hipStream_t>(stream));
+  return r < 0 ? FA_ERR_HIP : r != 0 ? FA_ERR_INVALID_ARG : FA_OK;
+#else
+  (void)c;
+  (void)stream;
+  return FA_OK;
+#endif
+}
+
+fa::DeviceChecks varlen_checks(const int* cu_q, const int* cu_k, int B, int total_q, int total_k,
+                               int max_q, int max_k) {
+  fa::DeviceChecks c = {};
+  c.cu_q = cu_q; c.cu_k = cu_k; c.B = B;
+  c.total_q = total_q; c.total_k = total_k; c.max_q = max_q; c.max_k = max_k;
+  return c;
+}
+
+fa::DeviceChecks paged_checks(const int* block_table, const int* seqlens, int B, int max_blocks,
+                              int page_size, int num_pages, int extra_len) {
+  fa::DeviceChecks c = {};
+  c.block_table = block_table; c.seqlens = seqlens; c.B = B;
+  c.max_blocks = max_blocks; c.page_size = page_size; c.num_pages = num_pages;
+  c.extra_len = extra_len;
+  return c;
+}
 
 fa_status check_common(int Hq, int Hkv, int d, float scale, int causal, int wl, int wr) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
@@ -189,6 +222,9 @@ fa_status varlen_impl(const void* q, const void* k, const void* v, void* o, floa
   p.xcd_groups = xcd_groups(Hkv);
   if ((int64_t)p.num_q_tiles * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
   if (p.num_q_tiles == 0) return FA_OK;
+  st = device_checks(varlen_checks(cu_seqlens_q, cu_seqlens_k, B, total_q, total_k, max_seqlen_q,
+                                   max_seqlen_k), stream);
+  if (st != FA_OK) return st;
   hipError_t e = fa::launch_prefill(p, d, 1, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -250,7 +286,12 @@ fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
   if ((int64_t)page_size * Hkv * d * 2 >= ((int64_t)1 << 30)) return FA_ERR_INVALID_ARG;
   if ((int64_t)Lq * Hq * d >= kMaxBatchElems) return FA_ERR_INVALID_ARG;
   if ((int64_t)max_blocks_per_seq * page_size >= ((int64_t)1 << 30)) return FA_ERR_INVALID_ARG;
+  if (cdiv(Lq, fa::kBlockM) * B * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
+  if (k_new && B > 65535) return FA_ERR_INVALID_ARG;   // append grid (Lq, B)
   if (Lq == 0) return FA_OK;
+  st = device_checks(paged_checks(block_table, cache_seqlens, B, max_blocks_per_seq, page_size,
+                                  num_pages, k_new ? Lq : 0), stream);
+  if (st != FA_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (k_new) {
@@ -263,7 +304,6 @@ fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
     a.cache_seqlens = cache_seqlens;
     a.B = B; a.L_new = Lq; a.Hkv = Hkv; a.d = d;
     a.page_size = page_size; a.max_blocks = max_blocks_per_seq;
-    if (B > 65535) return FA_ERR_INVALID_ARG;   // append grid (Lq, B)
     if (fa::launch_append(a, s) != hipSuccess) return FA_ERR_HIP;
   }
 
@@ -286,7 +326,6 @@ fa_status fa_fwd_kvcache(const void* q, void* k_cache, void* v_cache,
   p.num_q_tiles = (int)cdiv(Lq, fa::kBlockM);
   p.xcd_groups = xcd_groups(B * Hkv);
   p.chunk_groups = (int)std::max<int64_t>(1, fa::kPrefillSlotsPerXcd / ((int64_t)p.group * p.num_q_tiles));
-  if ((int64_t)p.num_q_tiles * B * Hq >= kMaxElems) return FA_ERR_INVALID_ARG;
   p.block_table = block_table;
   p.cache_seqlens = cache_seqlens;
   p.page_size = page_size;
@@ -397,6 +436,9 @@ fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   p.alibi = alibi_slopes;
   p.alibi_bstride = alibi_slopes ? alibi_batch_stride : 0;
   p.alibi_scale = 1.f / softmax_scale;
+  st = device_checks(paged_checks(block_table, cache_seqlens, B, max_blocks_per_seq, page_size,
+                                  num_pages, 0), stream);
+  if (st != FA_OK) return st;
   hipError_t e = fa::launch_decode(p, d, rows, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -578,6 +620,9 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
   p.xcd_groups = xcd_groups(Hkv);
   if ((int64_t)p.num_q_tiles * Hq >= kMaxElems || (int64_t)p.num_k_tiles * Hkv >= kMaxElems)
     return FA_ERR_INVALID_ARG;
+  st = device_checks(varlen_checks(cu_seqlens_q, cu_seqlens_k, B, total_q, total_k, max_seqlen_q,
+                                   max_seqlen_k), stream);
+  if (st != FA_OK) return st;
   hipError_t e = fa::launch_bwd(p, d, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

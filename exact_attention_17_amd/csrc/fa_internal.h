@@ -148,4 +148,25 @@ void* decode_scratch(hipError_t* err);
 // row statistics, then dK/dV, then dQ, in stream order
 hipError_t launch_bwd(const BwdParams& p, int d, bool varlen, hipStream_t stream);
 
+// Device-side preconditions that the host cannot see (debug builds only,
+// -DFA_DEBUG).  Varlen: cu_q / cu_k (B + 1 entries) start at 0, never
+// decrease, end at total_q / total_k, and no sequence is longer than
+// max_q / max_k.  Paged: each request's key count n_b = seqlens[b] +
+// extra_len lies in [extra_len, max_blocks * page_size] and the first
+// ceil(n_b / page_size) entries of its block-table row lie in
+// [0, num_pages).  A null cu_q (block_table) skips the varlen (paged) part.
+struct DeviceChecks {
+  const int* cu_q; const int* cu_k;
+  int total_q, total_k, max_q, max_k;
+  const int* block_table; const int* seqlens;
+  int max_blocks, page_size, num_pages, extra_len;
+  int B;
+};
+// Runs the checks on `stream` and waits for them: 0 when they hold, a
+// non-zero mask of the violated groups (1 varlen offsets, 2 key counts,
+// 4 page ids) otherwise, -1 if a HIP call failed.  Allocates nothing (the
+// result goes through a device word of the library); it waits for the
+// stream, so it is not for code under graph capture.
+int debug_check_inputs(const DeviceChecks& c, hipStream_t stream);
+
 }  // namespace fa

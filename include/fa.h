@@ -50,7 +50,11 @@
  *     preconditions that cannot be checked without reading device memory
  *     (monotone cu_seqlens ending at total, block_table entries in
  *     [0, num_pages) for the pages a request uses, cache_seqlens[b] <=
- *     max_blocks_per_seq * page_size) are the caller's responsibility.
+ *     max_blocks_per_seq * page_size) are the caller's responsibility.  The
+ *     debug build of this library (compiled with -DFA_DEBUG) checks them on
+ *     the device, after the host checks and before any other work is
+ *     enqueued, and returns FA_ERR_INVALID_ARG when one fails; its calls
+ *     wait for their stream, so they cannot be captured in a graph.
  *   - Calls are reentrant and thread-safe: the library has no global state,
  *     except the per-GPU scratch array of fa_decode_paged_noalloc (see there).
  */
@@ -292,7 +296,7 @@ fa_status fa_decode_paged_noalloc(const void* q, const void* k_cache, const void
  *   cache_seqlens : device int32 [B]: keys already in the cache.  Request b
  *       attends to n_b = cache_seqlens[b] (+ Lq when appending) keys, with
  *       n_b <= max_blocks_per_seq * page_size and the first ceil(n_b /
- *       page_size) table entries valid (not checked on the device).
+ *       page_size) table entries valid (checked only by the debug build).
  *   lse      : (B, Hq, Lq) float32, or NULL.
  *   causal, window_left, window_right : as fa_fwd, with query row i at key
  *       position i + n_b - Lq (bottom-right).

@@ -108,3 +108,111 @@ def test_debug_build_matches_release_chunked_prefill(debug_lib):
         return o, lse, kc, vc
     a, b = _both(debug_lib, call)
     _same(a, b)
+
+
+# ---- device-side preconditions (debug build only) ---------------------------
+# Each bad input below goes to the debug library alone, which must reject it
+# with FA_ERR_INVALID_ARG before any other kernel runs.  The inputs are laid
+# out so that even an unchecked read would stay inside mapped memory: the
+# page pool passed in is a slice of a larger one (page ids -1 and num_pages
+# exist), and over-long requests sit in row 0 of the block table.
+
+def _expect_invalid(libs, call):
+    saved = fa_mod._lib
+    fa_mod._lib = libs[1]
+    try:
+        with pytest.raises(fa_mod.FAError) as err:
+            call()
+        torch.cuda.synchronize()
+    finally:
+        fa_mod._lib = saved
+    assert err.value.status == 1
+
+
+def _paged_case():
+    p = workloads.random_paged(901, [300, 17, 650], 8, 2, 128, 16, 80, 256, max_blocks=48)
+    big_k = torch.cat([p.k_cache[:1], p.k_cache, p.k_cache[:1]]).cuda()
+    big_v = torch.cat([p.v_cache[:1], p.v_cache, p.v_cache[:1]]).cuda()
+    n = p.k_cache.shape[0]
+    return p, big_k[1:n + 1], big_v[1:n + 1], n
+
+
+@pytest.mark.gpu
+def test_debug_build_rejects_bad_page_ids_and_lengths(debug_lib):
+    p, kc, vc, n = _paged_case()
+    q = dev(p.q)
+    lens = dev(torch.as_tensor(p.seqlens))
+
+    def decode(table, sl):
+        return fa_mod.fa_decode_paged(q, kc, vc, dev(torch.as_tensor(table)), sl, p.scale, -1, 256)
+
+    # a valid call, and one with out-of-range ids only in entries past each
+    # request's pages (allowed), agree with the release library bit for bit
+    a, b = _both(debug_lib, lambda: decode(p.block_table, lens))
+    _same(a, b)
+    loose = p.block_table.copy()
+    for r, L in enumerate(p.seqlens):
+        loose[r, -(-int(L) // 16):] = 10 ** 6
+    a, b = _both(debug_lib, lambda: decode(loose, lens))
+    _same(a, b)
+    for bad_id in (-1, n):
+        t = p.block_table.copy()
+        t[0, 3] = bad_id
+        _expect_invalid(debug_lib, lambda: decode(t, lens))
+    long_lens = torch.as_tensor(p.seqlens).clone()
+    long_lens[0] = 48 * 16 + 1
+    _expect_invalid(debug_lib, lambda: decode(p.block_table, dev(long_lens)))
+    neg = torch.as_tensor(p.seqlens).clone()
+    neg[0] = -1
+    _expect_invalid(debug_lib, lambda: decode(p.block_table, dev(neg)))
+
+
+@pytest.mark.gpu
+def test_debug_build_rejects_bad_kvcache_before_appending(debug_lib):
+    w = workloads.random_kvcache(902, [300, 17], 64, 8, 2, 128, 16, True, True)
+    pool = w.k_cache.shape[0]
+    spare = torch.zeros((8,) + tuple(w.k_cache.shape[1:]), dtype=torch.bfloat16)
+    kc = torch.cat([w.k_cache, spare]).cuda()[:pool]
+    vc = torch.cat([w.v_cache, spare]).cuda()[:pool]
+    k0, v0 = kc.clone(), vc.clone()
+    table = w.block_table.copy()
+    table[0, 0] = pool + 5
+    sl = dev(torch.from_numpy(w.cache_seqlens))
+
+    def call(t, lens):
+        return fa_mod.fa_fwd_kvcache(dev(w.q), kc, vc, dev(torch.from_numpy(t)), lens, dev(w.k_new),
+                                     dev(w.v_new), w.scale, True)
+
+    _expect_invalid(debug_lib, lambda: call(table, sl))
+    # row 0 would need one token more than its table holds once the chunk is appended
+    over = torch.from_numpy(w.cache_seqlens.copy())
+    over[0] = w.block_table.shape[1] * 16 - 64 + 1
+    _expect_invalid(debug_lib, lambda: call(w.block_table, dev(over)))
+    torch.cuda.synchronize()
+    assert torch.equal(kc.view(torch.int16), k0.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), v0.view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_debug_build_rejects_bad_cu_seqlens(debug_lib):
+    w = workloads.random_varlen(903, [100, 200, 150], 4, 2, 64, True)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    good = w.cu_seqlens
+
+    def fwd(cu, mx=200):
+        c = dev(torch.from_numpy(np.asarray(cu, dtype=np.int32)))
+        return fa_mod.fa_fwd_varlen(q, k, v, c, c, mx, mx, w.scale, True)
+
+    a, b = _both(debug_lib, lambda: fwd(good))
+    _same(a, b)
+    for cu, mx in (([5, 100, 300, 450], 200),      # does not start at 0
+                   ([0, 200, 100, 450], 350),      # decreasing
+                   ([0, 100, 300, 440], 200),      # does not end at total
+                   ([0, 100, 300, 450], 150)):     # a sequence longer than max_seqlen
+        _expect_invalid(debug_lib, lambda: fwd(cu, mx))
+    o, lse = fwd(good)
+    do = dev(workloads.upstream_grad(904, tuple(w.q.shape)))
+    torch.cuda.synchronize()
+    short = dev(torch.from_numpy(np.asarray([0, 100, 300, 440], dtype=np.int32)))
+    _expect_invalid(debug_lib, lambda: fa_mod.fa_bwd_varlen(q, k, v, o, lse, do, short, short, 200,
+                                                            200, w.scale, True))
