@@ -235,6 +235,8 @@ def kvcache(lib, **kw):
     (dict(Hkv=3), INVALID), (dict(scale=float("nan")), INVALID), (dict(causal=5), INVALID),
     (dict(wl=-3), INVALID), (dict(ps=1 << 16, Hkv=64), INVALID), (dict(mb=1 << 26, ps=16), INVALID),
     (dict(cap=-2.0), INVALID), (dict(al=P + 1), INVALID),
+    # grid limits, checked before the append is enqueued (no HIP call here)
+    (dict(B=70000), INVALID), (dict(B=16384, Lq=(1 << 24) - 64, Hq=1, Hkv=1, d=64), INVALID),
 ])
 def test_kvcache_rejects(lib, kw, code):
     assert kvcache(lib, **kw) == code
