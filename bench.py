@@ -23,12 +23,16 @@ HBM bytes per launch from the committed rocprofv3 counter summary for that
 kernel and workload, null if the kernel source changed since it was taken.
 The causal MHA prefill (B=4, H=32, L=2048) and the paged decode call
 (fa_decode_paged, no host plan) carry roofline blocks of their own; the other
-workloads are reported under "workloads".  "cpu_baseline" times the CPU fp64
+workloads are reported under "workloads".  "hbm_context" gives the device
+memory bandwidth measured on this GPU beside the 8 TB/s spec (a streaming
+read by a probe kernel, and a device copy) and the decode rate as a fraction
+of that read rate (context only; the decode roofline stays against the spec).  "cpu_baseline" times the CPU fp64
 oracle on a bounded sample of the main workload on this host, and per
 workload under "cpu_baseline.per_workload".  One JSON line is printed.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -47,6 +51,7 @@ import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E (published)
+MEMBW_LIB = os.path.join(ROOT, "exact_attention_17_amd", "libfa_membw.so")
 METRIC = "prefill attn TFLOP/s (% MFMA peak); paged-decode KV GB/s (% HBM peak)"
 PREFILL_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "prefill_fwd.hip")
 WIDE_SRC = os.path.join(ROOT, "exact_attention_17_amd", "csrc", "prefill_wide.hip")
@@ -175,6 +180,51 @@ def copy_calibration(reps=5):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+
+
+def _event_median(fn, reps):
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return statistics.median([a.elapsed_time(b) for a, b in ev])
+
+
+def hbm_context(reps=20, nbytes=1 << 32):
+    """Device memory bandwidth measured on this GPU, as context for the 8 TB/s
+    spec: a streaming read of `nbytes` by the probe library (16-byte
+    non-temporal loads, best of four grid sizes) and torch's device-to-device
+    copy (bytes read + written).  Medians of `reps` event-timed calls."""
+    if not os.path.exists(MEMBW_LIB):
+        return {"error": "libfa_membw.so is not built"}
+    lib = ctypes.CDLL(MEMBW_LIB)
+    fn = lib.fa_membw_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    sink = torch.empty(16384 * 256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    per_grid = {}
+    for blocks in (2048, 4096, 8192, 16384):
+        def call(blocks=blocks):
+            if fn(src.data_ptr(), nbytes, sink.data_ptr(), blocks, stream) != 0:
+                raise RuntimeError("fa_membw_read failed")
+        per_grid[blocks] = round(nbytes / _event_median(call, reps) / 1e6, 1)
+    del sink
+    half = src[: src.numel() // 2]
+    dst = torch.empty_like(half)
+    copy = 2 * half.numel() * 4 / _event_median(lambda: dst.copy_(half), reps) / 1e6
+    del src, dst, half
+    return {"read_GB/s": max(per_grid.values()), "read_GB/s_by_grid": per_grid,
+            "copy_GB/s": round(copy, 1), "read_bytes": nbytes, "spec_GB/s": PEAK_HBM_GBS,
+            "kinds": "read: fa_membw_read (16-byte non-temporal loads); copy: torch copy_ "
+                     "(read + write)"}
 
 
 # ------------------------------------------------------------------ CPU oracle
@@ -516,6 +566,10 @@ def main():
     if only in (None, "decode"):
         dwl, result["roofline_decode"] = bench_decode(fa, args, extras=only is None)
         wl.update(dwl)
+        if only is None:
+            ctx = hbm_context()
+            ctx["decode_vs_read"] = round(result["roofline_decode"]["achieved"] / ctx["read_GB/s"], 4)
+            result["hbm_context"] = ctx
     if only in (None, "bwd"):
         wl.update(bench_bwd(fa, args, all_workloads=only is None))
     if only is None:

@@ -22,6 +22,10 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 # its destination with bf16 NaN, so a missing wait or barrier shows as NaN in
 # the outputs (tests/test_debug_build.py compares it with the release library).
 DEBUG_LIB_PATH = os.path.join(PKG_DIR, "libfa_debug.so")
+# A streaming-read bandwidth probe for the benchmark (its own library; the
+# attention library does not contain it).
+MEMBW_LIB_PATH = os.path.join(PKG_DIR, "libfa_membw.so")
+MEMBW_SOURCE = "membw.hip"
 SOURCES = ["fa_api.cpp", "plan.cpp", "prefill_fwd.hip", "prefill_wide.hip", "decode_paged.hip",
            "attn_bwd.hip", "debug_checks.hip"]
 ARCH = "gfx950"
@@ -34,22 +38,24 @@ def hipcc_path():
     raise RuntimeError("hipcc not found; the ROCm toolchain is required to build libfa.so")
 
 
-def compile_command(out=LIB_PATH, extra=()):
+def compile_command(out=LIB_PATH, extra=(), sources=SOURCES):
     cmd = [hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-command-line-argument",
            "-I", INCLUDE, "-I", CSRC, "-o", out]
     cmd += list(extra)
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += [os.path.join(CSRC, s) for s in sources]
     return cmd
 
 
-def build_library(verbose=False, extra=(), debug=False):
+def build_library(verbose=False, extra=(), debug=False, membw=False):
     """Compile every HIP source into LIB_PATH, or with debug=True into
-    DEBUG_LIB_PATH with -DFA_DEBUG (always recompiles)."""
-    target = DEBUG_LIB_PATH if debug else LIB_PATH
+    DEBUG_LIB_PATH with -DFA_DEBUG, or with membw=True the bandwidth probe
+    into MEMBW_LIB_PATH (always recompiles)."""
+    target = MEMBW_LIB_PATH if membw else DEBUG_LIB_PATH if debug else LIB_PATH
     tmp = target + ".tmp"
-    cmd = compile_command(tmp, list(extra) + (["-DFA_DEBUG"] if debug else []))
+    cmd = compile_command(tmp, list(extra) + (["-DFA_DEBUG"] if debug else []),
+                          [MEMBW_SOURCE] if membw else SOURCES)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,3 +73,4 @@ def build_library(verbose=False, extra=(), debug=False):
 if __name__ == "__main__":
     print(build_library(verbose=True))
     print(build_library(verbose=True, debug=True))
+    print(build_library(verbose=True, membw=True))

@@ -351,3 +351,18 @@ def test_bwd_varlen_workspace_size(lib):
     assert lib.fa_bwd_varlen_workspace_size(0, 4, 16) == 0
     # nothing to do: both totals 0 is accepted without a launch
     assert bwd_varlen(lib, tq=0, tk=0, mq=0, mk=0) == OK
+
+
+def test_membw_probe_rejects_bad_arguments():
+    """The benchmark's read-bandwidth probe (its own library) validates its
+    arguments on the host and enqueues nothing when they are bad."""
+    from exact_attention_17_amd import build
+    if not os.path.exists(build.MEMBW_LIB_PATH):
+        build.build_library(membw=True)
+    lib = ctypes.CDLL(build.MEMBW_LIB_PATH)
+    fn = lib.fa_membw_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    for src, nbytes, sink, blocks in [(None, 16, P, 1), (P, 0, P, 1), (P, 24, P, 1), (P + 8, 16, P, 1),
+                                      (P, 16, None, 1), (P, 16, P + 2, 1), (P, 16, P, 0)]:
+        assert fn(src, nbytes, sink, blocks, None) == 1
