@@ -568,7 +568,8 @@ def main():
         wl.update(dwl)
         if only is None:
             ctx = hbm_context()
-            ctx["decode_vs_read"] = round(result["roofline_decode"]["achieved"] / ctx["read_GB/s"], 4)
+            if "read_GB/s" in ctx:
+                ctx["decode_vs_read"] = round(result["roofline_decode"]["achieved"] / ctx["read_GB/s"], 4)
             result["hbm_context"] = ctx
     if only in (None, "bwd"):
         wl.update(bench_bwd(fa, args, all_workloads=only is None))
