@@ -133,6 +133,10 @@ FA_DEV void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soff
                :: "v"(voffset), "s"(r), "s"(soffset), "{m0}"(lds_base) : "memory");
 }
 FA_DEV void lds_load_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N of the wave's vector-memory loads are still in
+// flight.  Loads complete in issue order, so all but the last N have landed.
+template <int N>
+FA_DEV void lds_load_wait_n() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 // Forces the wait for a value from an ordinary (compiler-tracked) load at
 // this point.  A loop that also issues direct-to-LDS loads, which the compiler

@@ -160,7 +160,9 @@ void prefill_fwd_kernel(PrefillParams p) {
   const int kv_hi = key_hi(r_last);
   const int kt_begin = kv_lo / kBlockN;
   const int kt_end = kv_hi > kv_lo ? (kv_hi + kBlockN - 1) / kBlockN : kt_begin;
-  const int ntiles = kt_end - kt_begin;
+  // the loop runs the tiles in pairs: an odd count gets one more tile, past
+  // every row's last key (masked for all rows; rows at or past Lk load zeros)
+  const int ntiles = (kt_end - kt_begin + 1) & ~1;
 
   const int qw0 = q0 + 32 * wave;
   const int rw0 = min(qw0, Lq - 1), rw1 = min(qw0 + 31, Lq - 1);
@@ -373,16 +375,18 @@ void prefill_fwd_kernel(PrefillParams p) {
   // Instruction order of the step's main block: a few K fragment reads first,
   // then each MFMA followed by some softmax VALU ops and the next LDS reads,
   // so reads stay a few MFMAs ahead and the VALU work hides under the MFMAs.
-  auto interleave_hint = [](auto with_pv) {
+  auto interleave_hint = [](auto with_qk, auto with_pv) {
     // fixed schedule: K fragment reads issued up front, then per S^T MFMA
     // 4 VALU ops and 1 read, per P V MFMA 3 VALU ops and 2 reads
     constexpr int kReadsUp = 3, kValuQk = 4, kReadsQk = 1, kValuPv = 3, kReadsPv = 2;
     __builtin_amdgcn_sched_group_barrier(0x100, kReadsUp, 0);
+    if constexpr (decltype(with_qk)::value) {
 #pragma unroll
-    for (int i = 0; i < 2 * KSTEPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuQk, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, kReadsQk, 0);
+      for (int i = 0; i < 2 * KSTEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuQk, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kReadsQk, 0);
+      }
     }
     if constexpr (decltype(with_pv)::value) {
 #pragma unroll
@@ -410,12 +414,14 @@ void prefill_fwd_kernel(PrefillParams p) {
       lds_load16(qrs, q_src, (uint32_t)__builtin_amdgcn_readfirstlane(soff), v_lds_addr + wave_lds + 4096u * i);
     }
   }
-  if (ntiles > 0) {
+  if (ntiles > 0) {   // then ntiles >= 2
     const PageIds i0 = page_ids(kb0), i1 = page_ids(kb0 + kBlockN);
     fetch(krs, k_src, k_src_pg, kg, k_lds_addr, kb0, i0);
-    if (ntiles > 1) fetch(krs, k_src, k_src_pg, kg, k_lds_addr + TILE_BYTES, kb0 + kBlockN, i1);
+    fetch(krs, k_src, k_src_pg, kg, k_lds_addr + TILE_BYTES, kb0 + kBlockN, i1);
   }
-  lds_load_wait();
+  // S^T(0) needs Q and K(0) only: K(1) may still be in flight (its LOADS
+  // loads were issued last) until the barrier before step 0
+  if (ntiles > 0) lds_load_wait_n<LOADS>(); else lds_load_wait();
   __syncthreads();
   {
     const int rl = 32 * wave + n;
@@ -427,8 +433,9 @@ void prefill_fwd_kernel(PrefillParams p) {
   f32x16 s0[2], s1[2];
   u32x4 p0[4], p1[4];
   qk(0, s0);
-  // step 0 loads K(2) into K buffer 0 and V(0) over Q: every wave must be done
-  // reading K(0) and its Q rows
+  // step 0 reads K(1), loads K(2) into K buffer 0 and V(0) over Q: every wave
+  // must have its share of K(1) in LDS and be done reading K(0) and its Q rows
+  lds_load_wait();
   __syncthreads();
 
   // ---- main loop: two tiles per trip, ping-pong S and P registers ---------
@@ -441,11 +448,14 @@ void prefill_fwd_kernel(PrefillParams p) {
   // P_{j-1} cleared, so the block adds zeros.  Afterwards the max is taken
   // only when the tile shows a probability above 2^8 (rare).
   // Step 0 has no P_{-1}: its block holds only S^T(1) and the softmax of tile 0.
+  // The last step has no tile j+1: its block holds only P_{j-1} V_{j-1} (if
+  // any) and the softmax of tile j.
   // (the parity of j, and so every LDS buffer offset, is a compile-time constant)
-  auto step = [&](auto parity, auto first, int j, f32x16 (&Scur)[2], f32x16 (&Snxt)[2],
+  auto step = [&](auto parity, auto first, auto last, int j, f32x16 (&Scur)[2], f32x16 (&Snxt)[2],
                   u32x4 (&Pprev)[4], u32x4 (&Pcur)[4]) {
     constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
     constexpr bool FIRST = decltype(first)::value;   // no P_{j-1} V_{j-1} before tile 0
+    constexpr bool LAST = decltype(last)::value;     // no S^T(j+1) after the last tile
     const int kb = kb0 + j * kBlockN;
     modify(Scur, kb);
     mask_tile(Scur, kb);
@@ -468,10 +478,10 @@ void prefill_fwd_kernel(PrefillParams p) {
     ids_k = page_ids(kb + 3 * kBlockN);
     ids_v = page_ids(kb + kBlockN);
     const float la0 = l_a, lb0 = l_b;
-    qk(nxt, Snxt);
+    if constexpr (!LAST) qk(nxt, Snxt);
     if constexpr (!FIRST) pv(nxt, Pprev);
     softmax(Scur, Pcur);
-    interleave_hint(std::integral_constant<bool, !FIRST>{});
+    interleave_hint(std::integral_constant<bool, !LAST>{}, std::integral_constant<bool, !FIRST>{});
     // this lane's share of the tile's row sum bounds each of its probabilities
     // (also catches inf/NaN): above 2^8, take back the tile, raise the max and
     // rescale (P_{j-1} V_{j-1} is already in O, relative to the old max), and
@@ -487,14 +497,21 @@ void prefill_fwd_kernel(PrefillParams p) {
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  if (ntiles > 0) step(P0{}, std::true_type{}, 0, s0, s1, p1, p0);
-  for (int j = 1; j < ntiles; j += 2) {
-    step(P1{}, std::false_type{}, j, s1, s0, p0, p1);
-    if (j + 1 < ntiles) step(P0{}, std::false_type{}, j + 1, s0, s1, p1, p0);
-  }
-  // the last tile's P V
+  using T = std::true_type;
+  using F = std::false_type;
+  // ntiles is even: step 0, pairs of steps, and the last step (odd parity)
   if (ntiles > 0) {
-    if ((ntiles - 1) & 1) pv(1, p1); else pv(0, p0);
+    step(P0{}, T{}, F{}, 0, s0, s1, p1, p0);
+    for (int j = 1; j + 1 < ntiles; j += 2) {
+      step(P1{}, F{}, F{}, j, s1, s0, p0, p1);
+      step(P0{}, F{}, F{}, j + 1, s0, s1, p1, p0);
+    }
+    step(P1{}, F{}, T{}, ntiles - 1, s1, s0, p0, p1);
+    // the last tile's P V, unless no row of this wave sees a key of that
+    // tile (its P is zero: the causal diagonal of the wave's earlier rows, or
+    // the extra tile of an odd count)
+    const int kb_last = kb0 + (ntiles - 1) * kBlockN;
+    if (kb_last < key_hi(rw1) && kb_last + kBlockN > key_lo(rw0)) pv(1, p1);
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2 ------------
