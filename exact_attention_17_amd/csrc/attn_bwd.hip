@@ -557,6 +557,7 @@ void bwd_dq_kernel(BwdParams p) {
   const int qw0 = q0 + 32 * wave;
   const int rw0 = min(qw0, Lq - 1), rw1 = min(qw0 + 31, Lq - 1);
   const int wlo_last = key_lo(rw1), whi_first = key_hi(rw0);
+  const int wlo_first = key_lo(rw0), whi_last = key_hi(rw1);
   const int row = qw0 + n;
   const int my_lo = key_lo(row), my_hi = key_hi(row);
 
@@ -641,8 +642,13 @@ void bwd_dq_kernel(BwdParams p) {
     if (j + 1 < ntiles) fetch(kb + kBlockN, cur ^ 1);
     const char* kt_b = k_lds_b + cur * TILE_BYTES;
     const char* vt_b = v_lds_b + cur * TILE_BYTES;
+    // a tile none of whose keys any row of this wave sees adds nothing to
+    // its dQ (on the causal diagonal, the workgroup's first rows): the wave
+    // only takes part in the tile's loads and barrier
+    const bool none = kb >= whi_last || kb + kBlockN <= wlo_first;
     const bool full = kb >= wlo_last && kb + kBlockN <= whi_first;
     const int klo = my_lo - kb - 4 * hi, kspan = max(my_hi - my_lo, 0);
+    if (!none) {
     u32x4 dsf[4];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -674,6 +680,7 @@ void bwd_dq_kernel(BwdParams p) {
     for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) dqa[db] = mfma32x32x16(tr_frag(kt_b, cc, db), dsf[cc], dqa[db]);
+    }
     }
     lds_load_wait();
     __syncthreads();
