@@ -367,8 +367,8 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
   // (0..63) is score 2 r2 + (e & 1) of pair i = e / 2 (block (qb, kh) = i / 8 in
   // the order (0,0) (1,0) (0,1) (1,1), r2 = i % 8).  Slot s finishes element s
   // (row-sum add; the pack of the pair on odd e), takes the exponential of
-  // element s + 1 and scales element s + 2, so no instruction of a slot waits
-  // for another of the same slot.
+  // element s + 3 and scales element s + 4, so no instruction waits for
+  // another of its own slot and each exponential has three slots to finish.
   auto el_a = [&](const f32x16 (&Sc)[QB][2], float (&xs)[64], auto ec) __attribute__((always_inline)) {
     constexpr int e = decltype(ec)::value;
     if constexpr (e < 64) {
@@ -475,7 +475,11 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
     float xs[64], ps[64];
     el_a(Sc, xs, std::integral_constant<int, 0>{});
     el_a(Sc, xs, std::integral_constant<int, 1>{});
+    el_a(Sc, xs, std::integral_constant<int, 2>{});
+    el_a(Sc, xs, std::integral_constant<int, 3>{});
     el_b(xs, ps, std::integral_constant<int, 0>{});
+    el_b(xs, ps, std::integral_constant<int, 1>{});
+    el_b(xs, ps, std::integral_constant<int, 2>{});
     sched_fence();
     static_for<0, 64>([&](auto slot) __attribute__((always_inline)) {
       constexpr int s = decltype(slot)::value;
@@ -496,8 +500,8 @@ void prefill_fwd_wide_kernel(PrefillParams p) {
         mma_o(oacc[qb][g & 3], vf[g & 1], Pp[qb][g >> 2]);
       }
       el_c(ps, Pc, std::integral_constant<int, s>{});
-      el_b(xs, ps, std::integral_constant<int, s + 1>{});
-      el_a(Sc, xs, std::integral_constant<int, s + 2>{});
+      el_b(xs, ps, std::integral_constant<int, s + 3>{});
+      el_a(Sc, xs, std::integral_constant<int, s + 4>{});
       // The step's tile loads ride in the first half of the block, one 1 KB
       // load every 4 slots: K(j+2) into the buffer of K(j) and V(j) into that
       // of V(j-2), both last read in step j-1.  Spread this way their issue
