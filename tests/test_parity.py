@@ -52,6 +52,11 @@ DENSE_CASES = [
     (1, 33, 1, 2, 1, 64, False, (-1, -1)),         # one key
     (2, 190, 190, 6, 3, 128, True, (0, 0)),        # window (0, 0): self only
     (1, 160, 160, 4, 2, 64, False, (-1, -1)),
+    # odd key-tile counts whose extra (padding) tile holds real keys no row
+    # sees (most of the workgroups of these shapes)
+    (1, 640, 640, 2, 1, 128, False, (100, 30)),
+    (1, 900, 900, 4, 2, 128, True, (40, 0)),
+    (1, 900, 900, 2, 2, 64, True, (10, 0)),
 ]
 
 
