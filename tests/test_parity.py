@@ -137,6 +137,35 @@ def test_varlen_sweep(fa, case):
     check(f"varlen{case}", o.cpu(), lse.cpu(), O, LSE)
 
 
+
+VARLEN_QK_CASES = [
+    # query lengths, key lengths, Hq, Hkv, d, causal, window
+    ([100, 0, 260, 7], [300, 50, 260, 1], 4, 2, 128, True, (-1, -1)),   # chunks over longer prefixes; no rows
+    ([300, 40, 129], [0, 400, 64], 4, 1, 64, True, (64, -1)),           # no keys; Lq > Lk
+    ([65, 200], [900, 333], 8, 8, 128, False, (100, 20)),                # two-sided window, Lq < Lk
+    ([128, 1], [1000, 1], 2, 2, 64, True, (0, 0)),                       # self only
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_QK_CASES, ids=lambda c: f"n{len(c[0])}-h{c[2]}-kv{c[3]}-d{c[4]}-c{int(c[5])}-w{c[6][0]}_{c[6][1]}")
+def test_varlen_separate_query_key_lengths(fa, case):
+    """Packed sequences whose query and key counts differ (cu_seqlens_q != cu_seqlens_k):
+    the causal mask aligns each sequence's last query with its last key."""
+    lq, lk, Hq, Hkv, d, causal, window = case
+    q, k, v, cq, ck = workloads.random_varlen_qk(1300 + sum(lq) + sum(lk) + d, lq, lk, Hq, Hkv, d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.fa_fwd_varlen(dev(q), dev(k), dev(v), dev(torch.from_numpy(cq)), dev(torch.from_numpy(ck)),
+                              max(lq), max(lk), scale, causal, window)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention_varlen_ref(bits(q), bits(k), bits(v), cq, ck, scale, causal, window)
+    check(f"varlen_qk{case}", o.cpu(), lse.cpu(), O, LSE)
+    # the planned run over the same batch gives the same bits
+    plan = dev(torch.from_numpy(np.ascontiguousarray(fa.fa_varlen_plan(cq, ck, causal, window))))
+    o2, lse2 = fa.fa_fwd_varlen_run(dev(q), dev(k), dev(v), dev(torch.from_numpy(cq)),
+                                    dev(torch.from_numpy(ck)), plan, max(lq), max(lk), scale, causal, window)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+
 # -------------------------------------------------------------------- decode
 def run_decode(fa, w, split=None, window_left=None):
     out = fa.fa_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache),
