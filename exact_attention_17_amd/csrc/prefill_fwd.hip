@@ -95,8 +95,8 @@ template <int D> struct Lds {
 // keys from a paged KV cache.
 // MODS: softcap and/or ALiBi requested (a separate instance, so the plain
 // kernel carries none of their registers).
-// Occupancy: two workgroups per CU at d = 128 (236 VGPRs); three at d = 64,
-// where 168 VGPRs suffice apart from a few values spilled around the loop.
+// Occupancy: two workgroups per CU at d = 128 (235 VGPRs); three at d = 64
+// (164 VGPRs, within the 168 that three workgroups allow).
 template <int D, int MODE, bool MODS>
 __global__ __launch_bounds__(kPrefillThreads, D == 64 ? 3 : 2)
 void prefill_fwd_kernel(PrefillParams p) {
