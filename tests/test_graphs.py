@@ -111,39 +111,3 @@ def test_graph_backward(fa):
     g = capture(lambda: fa.fa_bwd(q, k, v, o, lse, do, w.scale, True, dq=dq, dk=dk, dv=dv, workspace=ws))
     replay_and_compare(g, [dq, dk, dv], ref)
 
-
-def test_side_stream_calls_match_eager(fa):
-    """Calls on a stream other than the current one allocate their outputs and
-    workspaces on that stream: the memory stays with the launch stream's pool
-    while its kernels run, so allocations and writes on the current stream right
-    after the call cannot reach it.  Each result is compared bitwise with the same
-    call made eagerly on the current stream."""
-    w = workloads.random_dense(67, 2, 500, 500, 8, 2, 128, True, (-1, -1))
-    q, k, v = dev(w.q), dev(w.k), dev(w.v)
-    do = workloads.device_normal(68, tuple(q.shape), "cuda")
-    p = workloads.random_paged(69, [900, 17, 1500, 3], 32, 8, 128, 16, 200, 512, max_blocks=100)
-    qd, kc, vc = dev(p.q), dev(p.k_cache), dev(p.v_cache)
-    bt, sl = dev(torch.from_numpy(p.block_table)), dev(torch.from_numpy(p.seqlens))
-
-    def calls(stream):
-        o, lse = fa.fa_fwd(q, k, v, w.scale, True, stream=stream)
-        grads = fa.fa_bwd(q, k, v, o, lse, do, w.scale, True, stream=stream)
-        od, ld = fa.fa_decode_paged(qd, kc, vc, bt, sl, p.scale, -1, 512, stream=stream)
-        return [o, lse, *grads, od, ld]
-
-    ref = [t.clone() for t in calls(None)]
-    torch.cuda.synchronize()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    busy = torch.randn(4096, 4096, device="cuda")
-    with torch.cuda.stream(side):
-        for _ in range(8):                      # delay the side stream's kernels
-            busy = busy @ busy * 1e-3
-    got = calls(side)
-    # allocations and writes on the current stream while the side stream runs
-    clobber = [torch.full((1 << 22,), 7.0, device="cuda") for _ in range(8)]
-    side.synchronize()
-    torch.cuda.synchronize()
-    del clobber
-    for g_, r in zip(got, ref):
-        assert torch.equal(g_, r)

@@ -145,7 +145,11 @@ def test_side_stream_calls_match_current_stream_calls(fa):
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
+    busy = torch.randn(4096, 4096, device="cuda")
     for _ in range(3):
+        with torch.cuda.stream(side):
+            for _ in range(4):                  # delay the side stream's kernels, so the
+                busy = busy @ busy * 1e-3       # current stream's writes below overlap them
         f = fa.fa_fwd(q, k, v, w.scale, True, stream=side)
         d = fa.fa_decode_paged(pq, kc, vc, bt, sl, p.scale, -1, 512, stream=side)
         g = fa.fa_bwd(q, k, v, ref_f[0], ref_f[1], do, w.scale, True, stream=side)
